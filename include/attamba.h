@@ -1,0 +1,250 @@
+/*
+ * attamba.h — C ABI of the Attamba KV-SSM forward on AMD Instinct MI355X (gfx950).
+ *
+ * The method is Attamba ("Attending To Multi-Token States", arXiv 2411.17685): two selective
+ * state-space scans SSM_K and SSM_V take the place of the key and value projections and
+ * compress every chunk of P tokens into one boundary state; attention then runs over the
+ * boundary states of completed chunks, the current partial chunk (M_train) and the L most
+ * recent uncompressed tokens (M_test plus sliding window); decoding keeps a cache of
+ * boundary states. Page references: pith.science review of the paper, sections "What carries
+ * the argument", "Core claim", "If this is right", "Assumptions & free parameters" and the
+ * Referee Report; rohan-paul.com summary, "Solution in this Paper" and "Key Insights".
+ *
+ * Conventions for every entry point:
+ *  - Return value: ATTAMBA_OK (0) or one of the ATTAMBA_ERR_* codes. On error nothing has
+ *    been launched, and attamba_last_error() (thread-local) describes the first failing
+ *    check. Argument checks are host-side and synchronous; kernels never trap.
+ *  - Tensors are caller-owned, contiguous, row-major device pointers unless named *_host.
+ *    The library allocates no device memory and keeps no state between calls; work that
+ *    needs scratch takes a caller-provided workspace.
+ *  - Device index arrays (seq_cu, chunk_cu, token_chunk) must be well formed (offsets
+ *    non-decreasing, starting at 0, ending at T; every sequence start is a chunk start);
+ *    that is the caller's contract. Kernels bound every write by the sizes passed here.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the default
+ *    stream); no call synchronises the host with the device.
+ *  - Activations are ATTAMBA_FP32 or ATTAMBA_BF16; SSM parameters (A, D, dt bias) are
+ *    always float32. Arithmetic is float32 throughout (state, exponentials, softmax and
+ *    accumulation); bf16 outputs are rounded to nearest even.
+ */
+#ifndef ATTAMBA_H
+#define ATTAMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* attamba_stream_t; /* hipStream_t */
+
+enum {
+  ATTAMBA_OK = 0,
+  ATTAMBA_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+  ATTAMBA_ERR_BAD_SHAPE = 2,   /* sizes negative, inconsistent, or index data malformed */
+  ATTAMBA_ERR_BAD_DTYPE = 3,   /* unknown dtype code */
+  ATTAMBA_ERR_CAPACITY = 4,    /* an output buffer is too small for the result */
+  ATTAMBA_ERR_UNSUPPORTED = 5, /* valid but not built (state size, head dim, width) */
+  ATTAMBA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+};
+
+enum { ATTAMBA_FP32 = 0, ATTAMBA_BF16 = 1 };
+
+/* M_train (paper Eq. 5): a query sees the boundary state of every completed chunk and the
+ * per-token outputs of its own partial chunk. M_test (Eq. 7, causal reading): it sees only
+ * boundary states of chunks that ended at or before it. Both add the window of the L most
+ * recent tokens (Eq. 8). pith.science "What carries the argument"; the Referee Report's
+ * second major comment explains why M_test must not expose the current chunk's final state
+ * before the chunk is complete. */
+enum { ATTAMBA_MASK_TRAIN = 0, ATTAMBA_MASK_TEST = 1 };
+
+const char* attamba_version(void);
+const char* attamba_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* attamba_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Segmentation (pith.science "What carries the argument": cyclic chunking shifts the chunk
+ * offset by layer index; "Assumptions & free parameters": offset = layer index; "If this is
+ * right": variable-length boundaries via cu_seqlens).
+ *
+ * Uniform chunking of a sequence of n tokens with o = layer_idx mod P: chunks start at local
+ * position 0 and at every t with t = o (mod P); the first chunk has length o when o > 0, a
+ * trailing partial chunk is a chunk. Chunks never cross sequences.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Host only. Number of chunks of the packed batch (S sequences, offsets seq_cu_host[S+1]):
+ * per sequence ceil(n/P) if o = 0, 1 + ceil((n-o)/P) if 0 < o < n, 1 if 0 < n <= o, 0 if
+ * n = 0. Errors: NULL_ARG; BAD_SHAPE if S < 0, P < 1, layer_idx < 0, seq_cu not starting at 0
+ * or decreasing, or the count exceeds INT32_MAX - 1. */
+int attamba_count_chunks(const int32_t* seq_cu_host, int32_t S, int32_t P, int32_t layer_idx,
+                         int32_t* n_chunks_out);
+
+/* Host only. Explicit (e.g. randomized) chunking: chunk_len_host[n_len] lists chunk lengths
+ * sequence by sequence; each is >= 1 and they tile every sequence exactly. Writes the chunk
+ * offsets chunk_cu_host_out[n_len + 1] (prefix sums). Errors: NULL_ARG; BAD_SHAPE if the
+ * lengths do not tile the sequences. */
+int attamba_chunk_cu_from_lengths(const int32_t* seq_cu_host, int32_t S,
+                                  const int32_t* chunk_len_host, int32_t n_len,
+                                  int32_t* chunk_cu_host_out);
+
+/* Device. Uniform chunking computed on the GPU from the device copy of seq_cu[S+1] over
+ * T tokens. Writes chunk_cu[n_chunks + 1] (chunk start offsets, then T), and, if not NULL,
+ * token_chunk[T] (chunk of every token) and is_end[T] (1 at the last token of every chunk,
+ * else 0). n_chunks must be the count attamba_count_chunks returns for the same seq_cu; the
+ * kernels never write past n_chunks + 1 entries. Errors: NULL_ARG (seq_cu, chunk_cu),
+ * BAD_SHAPE (S < 1, T < 0, P < 1, layer_idx < 0, n_chunks < 0), HIP. */
+int attamba_chunk_boundaries(const int32_t* seq_cu, int32_t S, int32_t T, int32_t P,
+                             int32_t layer_idx, int32_t n_chunks, int32_t* chunk_cu,
+                             int32_t* token_chunk, uint8_t* is_end, attamba_stream_t stream);
+
+/* Device. Per-token chunk index and chunk-end flags from device chunk offsets
+ * chunk_cu[n_chunks + 1] (any chunking, e.g. from attamba_chunk_cu_from_lengths). Either
+ * output may be NULL. Errors: NULL_ARG (chunk_cu), BAD_SHAPE (n_chunks < 0, T < 0), HIP. */
+int attamba_chunk_index(const int32_t* chunk_cu, int32_t n_chunks, int32_t T,
+                        int32_t* token_chunk, uint8_t* is_end, attamba_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * KV-SSM scan (pith.science "Core claim": K^(p) = SSM_K(X^(p)), V^(p) = SSM_V(X^(p)) per
+ * chunk; the selective SSM is the paper's Eq. 3, cited in "Assumptions & free parameters").
+ * For each SSM S in {K, V}, channel c and token t, with the state reset to zero at every
+ * chunk start:
+ *   delta = softplus(dt_S[t,c] + bias_S[c])
+ *   h[c,:] = exp(delta * A_S[c,:]) * h[c,:] + delta * x[t,c] * bm_S[t,:]
+ *   y_S[t,c] = sum_n cm_S[t,n] * h[c,n] + D_S[c] * x[t,c]
+ * The boundary state of chunk q is the output at its last token (the review's K^(p)[-1]).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t T;        /* tokens in the packed batch (>= 0) */
+  int32_t d;        /* channels = H * hd; multiple of 64 */
+  int32_t N;        /* state size per channel: 16 or 32 */
+  int32_t dtype;    /* activations: ATTAMBA_FP32 or ATTAMBA_BF16 */
+  int32_t n_chunks; /* chunks; chunk_cu has n_chunks + 1 entries */
+  const int32_t* chunk_cu;            /* [n_chunks + 1] device */
+  const void* x;                      /* [T, d] */
+  const void* dt_k;                   /* [T, d] step-size pre-activation (bias not added) */
+  const void* dt_v;                   /* [T, d] */
+  const void* bm_k;                   /* [T, N] input matrix of SSM_K */
+  const void* cm_k;                   /* [T, N] output matrix of SSM_K */
+  const void* bm_v;                   /* [T, N] */
+  const void* cm_v;                   /* [T, N] */
+  const float* A_k;                   /* [d, N] (negative entries) */
+  const float* A_v;                   /* [d, N] */
+  const float* D_k;                   /* [d] */
+  const float* D_v;                   /* [d] */
+  const float* bias_k;                /* [d] step-size bias */
+  const float* bias_v;                /* [d] */
+  void* y_k;                          /* [T, d] out: per-token keys, = [T, H, hd] */
+  void* y_v;                          /* [T, d] out: per-token values */
+  void* kb;                           /* [n_chunks, d] out or NULL: boundary keys */
+  void* vb;                           /* [n_chunks, d] out or NULL: boundary values */
+  /* Optional hand-off to decoding: the SSM states after the last token of each sequence. */
+  const int32_t* seq_cu;              /* [S + 1] device, or NULL */
+  int32_t S;
+  float* h_last_k;                    /* [S, d, N] out or NULL */
+  float* h_last_v;                    /* [S, d, N] out or NULL */
+} attamba_scan_args;
+
+/* Errors: NULL_ARG, BAD_SHAPE (T, n_chunks < 0; d not a positive multiple of 64),
+ * BAD_DTYPE, UNSUPPORTED (N not 16 or 32), HIP. */
+int attamba_kvssm_scan(const attamba_scan_args* args, attamba_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Chunk-aware causal attention over per-token and boundary keys (pith.science "What carries
+ * the argument": M_train Eq. 5, M_test Eq. 7, window Eq. 8; the map shrinks from n x n to
+ * about n/P + L keys per query).
+ * For query row i of a sequence starting at s0, with w_i = max(s0, i - L + 1) and, under
+ * M_train, w_i = min(w_i, start of i's chunk): the visible keys are the boundary states of
+ * the chunks that end before w_i plus the per-token keys at positions w_i..i. Each position
+ * counts once. O_i = softmax(scale * q_i . k_j) v_j over those keys; LSE_i = log of the
+ * softmax denominator (natural log). A row with no visible key gets O = 0, LSE = -inf.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t T;           /* tokens */
+  int32_t H;           /* heads (query heads = key/value heads) */
+  int32_t hd;          /* head dim: 32, 64 or 128 */
+  int32_t dtype;       /* q, k, v, kb, vb and out share this type */
+  int32_t S;           /* sequences; seq_cu has S + 1 entries */
+  int32_t max_seqlen;  /* upper bound on every sequence length (sizes the grid) */
+  int32_t n_chunks;
+  int32_t L;           /* leading tokens kept uncompressed (>= 0) */
+  int32_t mode;        /* ATTAMBA_MASK_TRAIN or ATTAMBA_MASK_TEST */
+  float scale;         /* softmax scale; 0 means 1/sqrt(hd) */
+  const void* q;       /* [T, H, hd] */
+  const void* k;       /* [T, H, hd] per-token keys (y_k) */
+  const void* v;       /* [T, H, hd] per-token values (y_v) */
+  const void* kb;      /* [n_chunks, H, hd] boundary keys */
+  const void* vb;      /* [n_chunks, H, hd] boundary values */
+  const int32_t* seq_cu;      /* [S + 1] device */
+  const int32_t* chunk_cu;    /* [n_chunks + 1] device */
+  const int32_t* token_chunk; /* [T] device */
+  void* out;           /* [T, H, hd] out */
+  float* lse;          /* [H, T] out or NULL */
+} attamba_attn_args;
+
+/* Errors: NULL_ARG, BAD_SHAPE (negative sizes, S < 1, max_seqlen < 1 with T > 0,
+ * L < 0, unknown mode), BAD_DTYPE, UNSUPPORTED (hd not 32/64/128), HIP. */
+int attamba_chunk_attn_fwd(const attamba_attn_args* args, attamba_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Decode step over a cache of boundary states (pith.science "Core claim": at inference only
+ * the final SSM state of each chunk is cached; "If this is right": the cache shrinks by
+ * about P, with L leading tokens kept). Uses M_test with the window. Every sequence of the
+ * batch is at the same position `pos`, with o = layer_idx mod P:
+ *   1. chunk start (pos = 0 or pos = o mod P): the SSM states are zeroed;
+ *   2. one SSM_K and SSM_V step gives the token's key and value (the recurrence above);
+ *   3. the key/value go to window slot pos mod L (if L > 0) and, if pos ends a chunk
+ *      ((pos + 1 - o) = 0 mod P), are appended as boundary state n_bound;
+ *   4. attention over boundary states 0 .. E-1, E = number of chunk ends before
+ *      w = max(0, pos - L + 1), plus the window positions w..pos;
+ *   5. pos and n_bound (host fields) advance.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t B, H, hd, d, N, P, L, layer_idx;
+  int32_t cap;         /* boundary-state capacity per sequence */
+  int32_t dtype;       /* cache, q, x, dt, bm/cm and out share this type */
+  int64_t pos;         /* host: position of the next token (same for all sequences) */
+  int32_t n_bound;     /* host: boundary states stored per sequence */
+  void* kb;            /* [B, H, cap, hd] boundary keys */
+  void* vb;            /* [B, H, cap, hd] boundary values */
+  void* kw;            /* [B, H, L, hd] window keys (slot = position mod L); NULL if L = 0 */
+  void* vw;            /* [B, H, L, hd] window values */
+  float* h_k;          /* [B, d, N] SSM_K state */
+  float* h_v;          /* [B, d, N] SSM_V state */
+  const float* A_k;    /* [d, N] */
+  const float* A_v;
+  const float* D_k;    /* [d] */
+  const float* D_v;
+  const float* bias_k; /* [d] */
+  const float* bias_v;
+  void* workspace;     /* device scratch of attamba_decode_workspace_size() bytes */
+  size_t workspace_bytes;
+} attamba_decode_cache;
+
+typedef struct {
+  const void* q;       /* [B, H, hd] */
+  const void* x;       /* [B, d] */
+  const void* dt_k;    /* [B, d] */
+  const void* dt_v;    /* [B, d] */
+  const void* bm_k;    /* [B, N] */
+  const void* cm_k;    /* [B, N] */
+  const void* bm_v;    /* [B, N] */
+  const void* cm_v;    /* [B, N] */
+  void* out;           /* [B, H, hd] out */
+} attamba_decode_inputs;
+
+/* Workspace bytes a decode step needs for this cache geometry (B, H, hd, cap, L); host only.
+ * Errors: NULL_ARG, BAD_SHAPE. */
+int attamba_decode_workspace_size(const attamba_decode_cache* cache, size_t* bytes);
+
+/* Errors: NULL_ARG; BAD_SHAPE (inconsistent sizes, pos < 0, n_bound not the number of chunk
+ * ends before pos); CAPACITY (an append would exceed cap, or the workspace is too small);
+ * BAD_DTYPE; UNSUPPORTED (hd not 32/64/128, N not 16/32, d not a multiple of 64); HIP.
+ * On success cache->pos and cache->n_bound are advanced. */
+int attamba_decode_step(attamba_decode_cache* cache, const attamba_decode_inputs* in,
+                        attamba_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTAMBA_H */

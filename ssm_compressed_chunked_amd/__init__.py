@@ -1,0 +1,13 @@
+"""Attamba KV-SSM forward on AMD Instinct MI355X (gfx950): HIP kernels behind a C ABI.
+
+The library libattamba.so (built in-tree by `python -m ssm_compressed_chunked_amd.build`)
+does all the work; this package is a thin ctypes binding over it with the same names as the
+C entry points (attamba_chunk_boundaries -> chunk_boundaries, and so on).
+"""
+from ._binding import (BF16, FP32, LIB_PATH, MASK_TEST, MASK_TRAIN, AttambaError, DecodeCache,
+                       chunk_attn_fwd, chunk_boundaries, chunk_cu_from_lengths, chunk_index,
+                       count_chunks, decode_step, kvssm_scan, lib, version)
+
+__all__ = ["BF16", "FP32", "LIB_PATH", "MASK_TEST", "MASK_TRAIN", "AttambaError", "DecodeCache",
+           "chunk_attn_fwd", "chunk_boundaries", "chunk_cu_from_lengths", "chunk_index",
+           "count_chunks", "decode_step", "kvssm_scan", "lib", "version"]

@@ -1,0 +1,236 @@
+// C ABI of libattamba: host-side argument checks, closed-form chunk counts, and the launches on
+// the caller's stream. Nothing here allocates device memory or synchronises with the device.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/attamba.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTAMBA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTAMBA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int32_t dt) { return dt == ATTAMBA_FP32 || dt == ATTAMBA_BF16; }
+
+// Chunks of one sequence of n tokens, offset o (uniform chunking with cyclic offset).
+int64_t chunks_of(int64_t n, int64_t P, int64_t o) {
+  if (n <= 0) return 0;
+  if (o == 0) return (n + P - 1) / P;
+  if (n <= o) return 1;
+  return 1 + (n - o + P - 1) / P;
+}
+
+// Chunk ends among positions 0 .. x-1 under the positional rule (j + 1 - o) = 0 (mod P).
+int64_t ends_before(int64_t x, int64_t P, int64_t o) {
+  if (x <= 0) return 0;
+  if (o == 0) return x / P;
+  return x >= o ? (x - o) / P + 1 : 0;
+}
+
+bool starts_chunk(int64_t pos, int64_t P, int64_t o) {
+  return pos == 0 || (((pos - o) % P) + P) % P == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attamba_version(void) { return "attamba-mi355x 0.1.0 (gfx950)"; }
+
+const char* attamba_status_string(int status) {
+  switch (status) {
+    case ATTAMBA_OK: return "ok";
+    case ATTAMBA_ERR_NULL_ARG: return "null argument";
+    case ATTAMBA_ERR_BAD_SHAPE: return "bad shape or index data";
+    case ATTAMBA_ERR_BAD_DTYPE: return "bad dtype";
+    case ATTAMBA_ERR_CAPACITY: return "capacity exceeded";
+    case ATTAMBA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTAMBA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attamba_last_error(void) { return g_last_error.c_str(); }
+
+int attamba_count_chunks(const int32_t* seq_cu_host, int32_t S, int32_t P, int32_t layer_idx,
+                         int32_t* n_chunks_out) {
+  if (!seq_cu_host || !n_chunks_out) return fail(ATTAMBA_ERR_NULL_ARG, "count_chunks: null pointer");
+  if (S < 0 || P < 1 || layer_idx < 0)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "count_chunks: S=%d P=%d layer_idx=%d", S, P, layer_idx);
+  if (seq_cu_host[0] != 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "count_chunks: seq_cu[0] != 0");
+  const int64_t o = layer_idx % P;
+  int64_t total = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t n = static_cast<int64_t>(seq_cu_host[s + 1]) - seq_cu_host[s];
+    if (n < 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "count_chunks: seq_cu decreases at %d", s);
+    total += chunks_of(n, P, o);
+  }
+  if (total > INT32_MAX - 1) return fail(ATTAMBA_ERR_BAD_SHAPE, "count_chunks: too many chunks");
+  *n_chunks_out = static_cast<int32_t>(total);
+  return ok();
+}
+
+int attamba_chunk_cu_from_lengths(const int32_t* seq_cu_host, int32_t S,
+                                  const int32_t* chunk_len_host, int32_t n_len,
+                                  int32_t* chunk_cu_host_out) {
+  if (!seq_cu_host || !chunk_cu_host_out || (n_len > 0 && !chunk_len_host))
+    return fail(ATTAMBA_ERR_NULL_ARG, "chunk_cu_from_lengths: null pointer");
+  if (S < 0 || n_len < 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_cu_from_lengths: S=%d n_len=%d", S, n_len);
+  if (seq_cu_host[0] != 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_cu_from_lengths: seq_cu[0] != 0");
+  int32_t k = 0;
+  int64_t pos = 0;
+  chunk_cu_host_out[0] = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t end = seq_cu_host[s + 1];
+    if (end < pos) return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_cu_from_lengths: seq_cu decreases at %d", s);
+    while (pos < end) {
+      if (k >= n_len) return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_cu_from_lengths: lengths end inside sequence %d", s);
+      const int64_t len = chunk_len_host[k];
+      if (len < 1 || pos + len > end)
+        return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_cu_from_lengths: chunk %d (length %lld) crosses sequence %d", k,
+                    static_cast<long long>(len), s);
+      pos += len;
+      chunk_cu_host_out[++k] = static_cast<int32_t>(pos);
+    }
+  }
+  if (k != n_len) return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_cu_from_lengths: %d lengths left over", n_len - k);
+  return ok();
+}
+
+int attamba_chunk_boundaries(const int32_t* seq_cu, int32_t S, int32_t T, int32_t P,
+                             int32_t layer_idx, int32_t n_chunks, int32_t* chunk_cu,
+                             int32_t* token_chunk, uint8_t* is_end, attamba_stream_t stream) {
+  if (!seq_cu || !chunk_cu) return fail(ATTAMBA_ERR_NULL_ARG, "chunk_boundaries: seq_cu/chunk_cu null");
+  if (S < 1 || T < 0 || P < 1 || layer_idx < 0 || n_chunks < 0 || n_chunks > T)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_boundaries: S=%d T=%d P=%d layer_idx=%d n_chunks=%d", S, T, P,
+                layer_idx, n_chunks);
+  return hip_status(attamba::launch_uniform_boundaries(seq_cu, S, T, P, layer_idx % P, n_chunks,
+                                                       chunk_cu, token_chunk, is_end,
+                                                       reinterpret_cast<hipStream_t>(stream)),
+                    "chunk_boundaries launch");
+}
+
+int attamba_chunk_index(const int32_t* chunk_cu, int32_t n_chunks, int32_t T,
+                        int32_t* token_chunk, uint8_t* is_end, attamba_stream_t stream) {
+  if (!chunk_cu) return fail(ATTAMBA_ERR_NULL_ARG, "chunk_index: chunk_cu null");
+  if (n_chunks < 0 || T < 0 || n_chunks > T || (T > 0 && n_chunks == 0))
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_index: n_chunks=%d T=%d", n_chunks, T);
+  return hip_status(attamba::launch_chunk_index(chunk_cu, n_chunks, T, token_chunk, is_end,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "chunk_index launch");
+}
+
+int attamba_kvssm_scan(const attamba_scan_args* a, attamba_stream_t stream) {
+  if (!a) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: args null");
+  if (!dtype_ok(a->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "kvssm_scan: dtype %d", a->dtype);
+  if (a->T < 0 || a->n_chunks < 0 || a->n_chunks > a->T || (a->T > 0 && a->n_chunks == 0))
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan: T=%d n_chunks=%d", a->T, a->n_chunks);
+  if (a->d <= 0 || a->d % 64 != 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan: d=%d not a positive multiple of 64", a->d);
+  if (a->N != 16 && a->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "kvssm_scan: N=%d (16 or 32)", a->N);
+  if (!a->chunk_cu || !a->x || !a->dt_k || !a->dt_v || !a->bm_k || !a->cm_k || !a->bm_v || !a->cm_v ||
+      !a->A_k || !a->A_v || !a->D_k || !a->D_v || !a->bias_k || !a->bias_v || !a->y_k || !a->y_v)
+    return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: a required pointer is null");
+  if (!a->kb != !a->vb) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: kb and vb must both be set or both null");
+  if (!a->h_last_k != !a->h_last_v) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: h_last_k/h_last_v must match");
+  if (a->h_last_k && (!a->seq_cu || a->S < 1))
+    return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: h_last needs seq_cu and S >= 1");
+  return hip_status(attamba::launch_kvssm_scan(*a, reinterpret_cast<hipStream_t>(stream)), "kvssm_scan launch");
+}
+
+int attamba_chunk_attn_fwd(const attamba_attn_args* a, attamba_stream_t stream) {
+  if (!a) return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_fwd: args null");
+  if (!dtype_ok(a->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "chunk_attn_fwd: dtype %d", a->dtype);
+  if (a->T < 0 || a->H < 1 || a->S < 1 || a->n_chunks < 0 || a->L < 0 ||
+      (a->T > 0 && (a->max_seqlen < 1 || a->n_chunks < 1)) ||
+      (a->mode != ATTAMBA_MASK_TRAIN && a->mode != ATTAMBA_MASK_TEST) || !(a->scale >= 0.0f))
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_attn_fwd: T=%d H=%d S=%d max_seqlen=%d n_chunks=%d L=%d mode=%d", a->T,
+                a->H, a->S, a->max_seqlen, a->n_chunks, a->L, a->mode);
+  if (a->hd != 32 && a->hd != 64 && a->hd != 128)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "chunk_attn_fwd: hd=%d (32, 64 or 128)", a->hd);
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->kb || !a->vb || !a->seq_cu || !a->chunk_cu ||
+                   !a->token_chunk || !a->out))
+    return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_fwd: a required pointer is null");
+  const float scale = a->scale > 0.0f ? a->scale : 1.0f / std::sqrt(static_cast<float>(a->hd));
+  return hip_status(attamba::launch_chunk_attn(*a, scale, reinterpret_cast<hipStream_t>(stream)),
+                    "chunk_attn_fwd launch");
+}
+
+int attamba_decode_workspace_size(const attamba_decode_cache* c, size_t* bytes) {
+  if (!c || !bytes) return fail(ATTAMBA_ERR_NULL_ARG, "decode_workspace_size: null pointer");
+  if (c->B < 1 || c->H < 1 || c->hd < 1 || c->cap < 0 || c->L < 0)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_workspace_size: B=%d H=%d hd=%d cap=%d L=%d", c->B, c->H, c->hd,
+                c->cap, c->L);
+  *bytes = attamba::decode_workspace_bytes(c->B, c->H, c->hd, c->cap, c->L);
+  return ok();
+}
+
+int attamba_decode_step(attamba_decode_cache* c, const attamba_decode_inputs* in,
+                        attamba_stream_t stream) {
+  if (!c || !in) return fail(ATTAMBA_ERR_NULL_ARG, "decode_step: null pointer");
+  if (!dtype_ok(c->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "decode_step: dtype %d", c->dtype);
+  if (c->B < 1 || c->H < 1 || c->P < 1 || c->L < 0 || c->layer_idx < 0 || c->cap < 0 || c->pos < 0 ||
+      c->n_bound < 0 || c->d != c->H * c->hd)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_step: B=%d H=%d hd=%d d=%d P=%d L=%d cap=%d pos=%lld", c->B, c->H,
+                c->hd, c->d, c->P, c->L, c->cap, static_cast<long long>(c->pos));
+  if (c->hd != 32 && c->hd != 64 && c->hd != 128)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_step: hd=%d (32, 64 or 128)", c->hd);
+  if (c->N != 16 && c->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_step: N=%d (16 or 32)", c->N);
+  if (c->d % 64 != 0) return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_step: d=%d not a multiple of 64", c->d);
+  if (!c->kb || !c->vb || !c->h_k || !c->h_v || !c->A_k || !c->A_v || !c->D_k || !c->D_v || !c->bias_k ||
+      !c->bias_v || !c->workspace || (c->L > 0 && (!c->kw || !c->vw)) || !in->q || !in->x || !in->dt_k ||
+      !in->dt_v || !in->bm_k || !in->cm_k || !in->bm_v || !in->cm_v || !in->out)
+    return fail(ATTAMBA_ERR_NULL_ARG, "decode_step: a required pointer is null");
+  const int64_t P = c->P, o = c->layer_idx % c->P, pos = c->pos;
+  if (ends_before(pos, P, o) != c->n_bound)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_step: n_bound=%d but %lld chunk ends precede pos=%lld", c->n_bound,
+                static_cast<long long>(ends_before(pos, P, o)), static_cast<long long>(pos));
+  attamba::DecodeLaunch dl{};
+  dl.pos = pos;
+  dl.is_start = starts_chunk(pos, P, o) ? 1 : 0;
+  dl.is_end = starts_chunk(pos + 1, P, o) ? 1 : 0;
+  if (dl.is_end && c->n_bound >= c->cap)
+    return fail(ATTAMBA_ERR_CAPACITY, "decode_step: boundary cache full (cap=%d)", c->cap);
+  if (c->workspace_bytes < attamba::decode_workspace_bytes(c->B, c->H, c->hd, c->cap, c->L))
+    return fail(ATTAMBA_ERR_CAPACITY, "decode_step: workspace of %zu bytes is too small", c->workspace_bytes);
+  dl.slot = c->L > 0 ? static_cast<int>(pos % c->L) : 0;
+  dl.n_bound_before = c->n_bound;
+  const int64_t w = c->L > 0 ? (pos - c->L + 1 > 0 ? pos - c->L + 1 : 0) : pos + 1;
+  dl.w = static_cast<int>(w);
+  dl.E = static_cast<int>(ends_before(w, P, o));
+  dl.n_window = c->L > 0 ? static_cast<int>(pos - w + 1) : 0;
+  dl.scale = 1.0f / std::sqrt(static_cast<float>(c->hd));
+  if (pos > INT32_MAX - 2) return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_step: pos too large");
+  const int st = hip_status(attamba::launch_decode_step(*c, *in, dl, reinterpret_cast<hipStream_t>(stream)),
+                            "decode_step launch");
+  if (st != ATTAMBA_OK) return st;
+  c->pos = pos + 1;
+  c->n_bound += dl.is_end;
+  return ATTAMBA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Device helpers shared by the HIP kernels of libattamba (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attamba {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kWave = 64;
+
+// Storage types: float32 or bf16 activations; arithmetic is always float32.
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(__bf16 v) { return static_cast<float>(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// gfx950 converts with v_cvt_pk_bf16_f32: round to nearest even.
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return static_cast<__bf16>(v); }
+
+// Hardware transcendental instructions: v_exp_f32 (2^x), v_log_f32 (log2 x), v_rcp_f32.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(z) = ln(1 + e^z). ln(1 + e) is taken as ln(w) * e / (w - 1) with w = 1 + e, which
+// keeps full relative accuracy when e is small (D. Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", 1991, Theorem 4); for z > 20 the result is z
+// to float32 precision.
+__device__ __forceinline__ float softplus_f32(float z) {
+  const float e = hw_exp2(z * kLog2e);
+  const float w = 1.0f + e;
+  const float r = (w == 1.0f) ? e : (hw_log2(w) * kLn2) * (e * hw_rcp(w - 1.0f));
+  return z > 20.0f ? z : r;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace attamba

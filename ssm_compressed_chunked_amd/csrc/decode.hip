@@ -1,0 +1,242 @@
+// Decode step over a cache of boundary states plus the L most recent tokens (pith.science
+// review of "Attamba: Attending To Multi-Token States", "Core claim": at inference only the
+// boundary states are cached; "If this is right": the cache shrinks by about P).
+//
+// Three launches on the caller's stream:
+//   1. decode_update: one lane per (sequence, channel): zero the state at a chunk start, one
+//      SSM_K and SSM_V step, write the token's key/value into its window slot and, at a chunk
+//      end, append it as the next boundary state;
+//   2. decode_attn_split: the key list of each (sequence, head) — boundary states 0..E-1 then
+//      window positions w..pos — is cut into splits of kSplit keys; each workgroup streams one
+//      split (16-byte loads, hd/8 lanes per key row, so one wave instruction reads several
+//      whole rows) and leaves an unnormalised partial (o, running max, sum) in the workspace;
+//   3. decode_combine: merges the partials of every (sequence, head).
+// The step is bound by HBM: the boundary cache is read once per step.
+#include "common.h"
+#include "kernels.h"
+
+namespace attamba {
+namespace {
+
+constexpr int kSplit = 256;          // keys per split workgroup
+constexpr int kSplitThreads = 256;
+
+template <typename T, int N>
+__global__ __launch_bounds__(kWave) void decode_update_kernel(attamba_decode_cache c,
+                                                              attamba_decode_inputs in,
+                                                              DecodeLaunch dl) {
+  const int b = blockIdx.y;
+  const int ch = blockIdx.x * kWave + threadIdx.x;
+  const int d = c.d;
+  const size_t bd = static_cast<size_t>(b) * d + ch;
+  const float x = to_f32(static_cast<const T*>(in.x)[bd]);
+  const int head = ch / c.hd, e = ch % c.hd;
+  auto run = [&](const float* A, const float* D, const float* bias, const T* dt, const T* bm,
+                 const T* cm, float* hstate) -> float {
+    const float delta = softplus_f32(to_f32(dt[bd]) + bias[ch]);
+    const float u = delta * x;
+    float* hp = hstate + bd * N;
+    const T* bmr = bm + static_cast<size_t>(b) * N;
+    const T* cmr = cm + static_cast<size_t>(b) * N;
+    float y = 0.f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const float inj = u * to_f32(bmr[n]);
+      const float hn = dl.is_start ? inj : fmaf(hw_exp2(delta * A[ch * N + n] * kLog2e), hp[n], inj);
+      hp[n] = hn;
+      y = fmaf(hn, to_f32(cmr[n]), y);
+    }
+    return fmaf(D[ch], x, y);
+  };
+  const float yk = run(c.A_k, c.D_k, c.bias_k, static_cast<const T*>(in.dt_k),
+                       static_cast<const T*>(in.bm_k), static_cast<const T*>(in.cm_k), c.h_k);
+  const float yv = run(c.A_v, c.D_v, c.bias_v, static_cast<const T*>(in.dt_v),
+                       static_cast<const T*>(in.bm_v), static_cast<const T*>(in.cm_v), c.h_v);
+  const size_t bh = static_cast<size_t>(b) * c.H + head;
+  if (c.L > 0) {
+    const size_t o = (bh * c.L + dl.slot) * c.hd + e;
+    static_cast<T*>(c.kw)[o] = from_f32<T>(yk);
+    static_cast<T*>(c.vw)[o] = from_f32<T>(yv);
+  }
+  if (dl.is_end) {
+    const size_t o = (bh * c.cap + dl.n_bound_before) * c.hd + e;
+    static_cast<T*>(c.kb)[o] = from_f32<T>(yk);
+    static_cast<T*>(c.vb)[o] = from_f32<T>(yv);
+  }
+}
+
+// Row pointer of key k of (b, h): boundary state k < E, else window position w + (k - E).
+template <typename T>
+__device__ __forceinline__ size_t key_row(const attamba_decode_cache& c, const DecodeLaunch& dl,
+                                          size_t bh, int k, bool& in_window) {
+  if (k < dl.E) {
+    in_window = false;
+    return (bh * c.cap + k) * c.hd;
+  }
+  in_window = true;
+  const int64_t pos = dl.w + (k - dl.E);
+  return (bh * c.L + static_cast<int>(pos % c.L)) * c.hd;
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
+    attamba_decode_cache c, attamba_decode_inputs in, DecodeLaunch dl, int max_splits) {
+  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte load
+  constexpr int LPK = HD / VEC;                // lanes per key row
+  constexpr int KPW = kWave / LPK;             // key rows per wave instruction
+  constexpr int NW = kSplitThreads / kWave;
+  constexpr int KPB = KPW * NW;                // key rows per workgroup iteration
+  __shared__ float s_p[kSplit];
+  __shared__ float s_red[NW];
+  __shared__ float s_acc[NW][KPW][HD];
+
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid % kWave, wid = tid / kWave;
+  const int sub = lane % LPK, grp = lane / LPK;
+  const size_t bh = static_cast<size_t>(b) * c.H + h;
+  const int n_keys = dl.E + dl.n_window;
+  const int k0 = sp * kSplit;
+  const int nk = min(kSplit, n_keys - k0);
+  float* part = static_cast<float*>(c.workspace) + (bh * max_splits + sp) * (HD + 2);
+
+  float qv[VEC];
+  {
+    const T* q = static_cast<const T*>(in.q) + bh * HD + sub * VEC;
+    const float qs = dl.scale * kLog2e;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) qv[v] = to_f32(q[v]) * qs;
+  }
+  const T* kbase = static_cast<const T*>(c.kb);
+  const T* kwin = static_cast<const T*>(c.kw);
+  const T* vbase = static_cast<const T*>(c.vb);
+  const T* vwin = static_cast<const T*>(c.vw);
+
+  // scores (log2 units)
+  for (int kk = wid * KPW + grp; kk < KPB * ceil_div(nk, KPB); kk += KPB) {
+    float sc = 0.f;
+    if (kk < nk) {
+      bool win;
+      const size_t row = key_row<T>(c, dl, bh, k0 + kk, win);
+      const T* kr = (win ? kwin : kbase) + row + sub * VEC;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) sc = fmaf(qv[v], to_f32(kr[v]), sc);
+    }
+#pragma unroll
+    for (int off = 1; off < LPK; off <<= 1) sc += __shfl_xor(sc, off, kWave);
+    if (sub == 0 && kk < nk) s_p[kk] = sc;
+  }
+  __syncthreads();
+  // max over the split
+  float mx = -INFINITY;
+  for (int k = tid; k < nk; k += kSplitThreads) mx = fmaxf(mx, s_p[k]);
+  for (int off = kWave / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+  if (lane == 0) s_red[wid] = mx;
+  __syncthreads();
+  mx = s_red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_red[w]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int k = tid; k < nk; k += kSplitThreads) {
+    const float pr = hw_exp2(s_p[k] - mx);
+    s_p[k] = pr;
+    sum += pr;
+  }
+  for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+  if (lane == 0) s_red[wid] = sum;
+  __syncthreads();
+  // P V
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  for (int kk = wid * KPW + grp; kk < nk; kk += KPB) {
+    bool win;
+    const size_t row = key_row<T>(c, dl, bh, k0 + kk, win);
+    const T* vr = (win ? vwin : vbase) + row + sub * VEC;
+    const float pr = s_p[kk];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = fmaf(pr, to_f32(vr[v]), acc[v]);
+  }
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) s_acc[wid][grp][sub * VEC + v] = acc[v];
+  __syncthreads();
+  for (int e = tid; e < HD; e += kSplitThreads) {
+    float o = 0.f;
+    for (int w = 0; w < NW; ++w)
+      for (int g = 0; g < KPW; ++g) o += s_acc[w][g][e];
+    part[e] = o;
+  }
+  if (tid == 0) {
+    float l = 0.f;
+    for (int w = 0; w < NW; ++w) l += s_red[w];
+    part[HD] = nk > 0 ? mx : -INFINITY;
+    part[HD + 1] = l;
+  }
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(HD) void decode_combine_kernel(attamba_decode_cache c,
+                                                            attamba_decode_inputs in,
+                                                            DecodeLaunch dl, int max_splits) {
+  const int h = blockIdx.x, b = blockIdx.y, e = threadIdx.x;
+  const size_t bh = static_cast<size_t>(b) * c.H + h;
+  const float* part = static_cast<const float*>(c.workspace) + bh * max_splits * (HD + 2);
+  float mx = -INFINITY;
+  for (int s = 0; s < dl.n_splits; ++s) mx = fmaxf(mx, part[s * (HD + 2) + HD]);
+  float o = 0.f, l = 0.f;
+  if (mx > -INFINITY) {
+    for (int s = 0; s < dl.n_splits; ++s) {
+      const float* ps = part + s * (HD + 2);
+      const float wgt = hw_exp2(ps[HD] - mx);
+      o = fmaf(ps[e], wgt, o);
+      l = fmaf(ps[HD + 1], wgt, l);
+    }
+  }
+  static_cast<T*>(in.out)[bh * HD + e] = from_f32<T>(l > 0.f ? o / l : 0.f);
+}
+
+template <typename T, int N, int HD>
+hipError_t launch_typed(const attamba_decode_cache& c, const attamba_decode_inputs& in,
+                        const DecodeLaunch& dl, hipStream_t stream) {
+  const int max_splits = decode_max_splits(c.cap, c.L);
+  hipLaunchKernelGGL((decode_update_kernel<T, N>), dim3(c.d / kWave, c.B), dim3(kWave), 0, stream,
+                     c, in, dl);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_attn_split_kernel<T, HD>), dim3(dl.n_splits, c.H, c.B),
+                     dim3(kSplitThreads), 0, stream, c, in, dl, max_splits);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_combine_kernel<T, HD>), dim3(c.H, c.B), dim3(HD), 0, stream, c, in,
+                     dl, max_splits);
+  return hipGetLastError();
+}
+
+template <typename T, int N>
+hipError_t launch_hd(const attamba_decode_cache& c, const attamba_decode_inputs& in,
+                     const DecodeLaunch& dl, hipStream_t stream) {
+  if (c.hd == 128) return launch_typed<T, N, 128>(c, in, dl, stream);
+  if (c.hd == 64) return launch_typed<T, N, 64>(c, in, dl, stream);
+  return launch_typed<T, N, 32>(c, in, dl, stream);
+}
+
+}  // namespace
+
+int decode_max_splits(int cap, int L) { return ceil_div(cap + L, kSplit) + 1; }
+
+size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L) {
+  return static_cast<size_t>(B) * H * decode_max_splits(cap, L) * (hd + 2) * sizeof(float);
+}
+
+hipError_t launch_decode_step(const attamba_decode_cache& c, const attamba_decode_inputs& in,
+                              const DecodeLaunch& dl_in, hipStream_t stream) {
+  DecodeLaunch dl = dl_in;
+  dl.n_splits = ceil_div(dl.E + dl.n_window, kSplit);
+  if (dl.n_splits == 0) dl.n_splits = 1;
+  if (c.dtype == ATTAMBA_BF16) {
+    return c.N == 16 ? launch_hd<__bf16, 16>(c, in, dl, stream) : launch_hd<__bf16, 32>(c, in, dl, stream);
+  }
+  return c.N == 16 ? launch_hd<float, 16>(c, in, dl, stream) : launch_hd<float, 32>(c, in, dl, stream);
+}
+
+}  // namespace attamba

@@ -1,0 +1,42 @@
+// Launchers of the HIP kernels; called by the C ABI layer after argument validation.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "../../include/attamba.h"
+
+namespace attamba {
+
+hipError_t launch_uniform_boundaries(const int32_t* seq_cu, int S, int T, int P, int o,
+                                     int n_chunks, int32_t* chunk_cu, int32_t* token_chunk,
+                                     uint8_t* is_end, hipStream_t stream);
+hipError_t launch_chunk_index(const int32_t* chunk_cu, int n_chunks, int T,
+                              int32_t* token_chunk, uint8_t* is_end, hipStream_t stream);
+// Attention kernel parameters (validated by the ABI layer).
+struct AttnParams {
+  int T, H, S, max_seqlen, L, train;
+  float scale;
+  const void *q, *k, *v, *kb, *vb;
+  const int32_t *seq_cu, *chunk_cu, *token_chunk;
+  void* out;
+  float* lse;
+};
+
+hipError_t launch_kvssm_scan(const attamba_scan_args& a, hipStream_t stream);
+hipError_t launch_chunk_attn(const attamba_attn_args& a, float scale, hipStream_t stream);
+
+struct DecodeLaunch {
+  int64_t pos;
+  int is_start, is_end;   // this position starts / ends a chunk
+  int slot;               // window slot pos mod L (L > 0)
+  int n_bound_before;     // boundary states stored before this step
+  int E;                  // boundary states attended (chunk ends before the window)
+  int n_window;           // window positions attended (pos - w + 1, or 0 if L = 0)
+  int w;                  // first window position
+  int n_splits;
+  float scale;
+};
+int decode_max_splits(int cap, int L);
+size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L);
+hipError_t launch_decode_step(const attamba_decode_cache& c, const attamba_decode_inputs& in,
+                              const DecodeLaunch& dl, hipStream_t stream);
+
+}  // namespace attamba

@@ -1,0 +1,102 @@
+"""The C ABI library loads, exports every entry point declared in include/attamba.h, and its
+host-side checks return the documented status codes before anything is launched (no GPU
+needed: every call below fails validation or is host-only)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ssm_compressed_chunked_amd as att
+from ssm_compressed_chunked_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attamba.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attamba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_exports_agree():
+    names = declared_functions()
+    assert len(names) == 11, names
+    assert set(names) == set(B.EXPORTS), (set(names) ^ set(B.EXPORTS))
+    lib = att.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {att.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_status_strings():
+    assert att.version().startswith("attamba-mi355x")
+    lib = att.lib()
+    assert lib.attamba_status_string(0) == b"ok"
+    assert lib.attamba_status_string(4) == b"capacity exceeded"
+    assert lib.attamba_status_string(99) == b"unknown status"
+
+
+def test_count_chunks_closed_form_and_errors():
+    assert att.count_chunks([0, 256], 4, 0) == 64
+    assert att.count_chunks([0, 2048, 4096, 6144, 8192], 8, 3) == 4 * 257
+    assert att.count_chunks([0, 5, 5, 17, 18], 4, 1) == 2 + 0 + 4 + 1
+    for bad in ([1, 5], [0, 5, 3]):
+        with pytest.raises(att.AttambaError) as e:
+            att.count_chunks(bad, 4, 0)
+        assert e.value.status == B.ERR_BAD_SHAPE
+    with pytest.raises(att.AttambaError):
+        att.count_chunks([0, 5], 0, 0)
+
+
+def test_chunk_cu_from_lengths():
+    np.testing.assert_array_equal(att.chunk_cu_from_lengths([0, 5, 9], [2, 3, 4]), [0, 2, 5, 9])
+    np.testing.assert_array_equal(att.chunk_cu_from_lengths([0, 0, 3], [3]), [0, 3])
+    for lens in ([2, 4, 3], [2, 3], [2, 3, 4, 1], [0, 5, 4]):
+        with pytest.raises(att.AttambaError) as e:
+            att.chunk_cu_from_lengths([0, 5, 9], lens)
+        assert e.value.status == B.ERR_BAD_SHAPE
+
+
+def test_device_entry_points_validate_before_launch():
+    lib = att.lib()
+    assert lib.attamba_kvssm_scan(None, None) == B.ERR_NULL_ARG
+    a = B.ScanArgs()
+    a.T, a.d, a.N, a.dtype, a.n_chunks = 16, 64, 16, 7, 4
+    assert lib.attamba_kvssm_scan(C.byref(a), None) == B.ERR_BAD_DTYPE
+    a.dtype = B.BF16
+    a.d = 96
+    assert lib.attamba_kvssm_scan(C.byref(a), None) == B.ERR_BAD_SHAPE
+    a.d, a.N = 64, 8
+    assert lib.attamba_kvssm_scan(C.byref(a), None) == B.ERR_UNSUPPORTED
+    a.N = 16
+    assert lib.attamba_kvssm_scan(C.byref(a), None) == B.ERR_NULL_ARG
+    assert b"required pointer" in lib.attamba_last_error()
+
+    t = B.AttnArgs()
+    t.T, t.H, t.hd, t.dtype, t.S, t.max_seqlen, t.n_chunks, t.L, t.mode = 8, 2, 48, 1, 1, 8, 2, 0, 1
+    assert lib.attamba_chunk_attn_fwd(C.byref(t), None) == B.ERR_UNSUPPORTED
+    t.hd, t.mode = 64, 5
+    assert lib.attamba_chunk_attn_fwd(C.byref(t), None) == B.ERR_BAD_SHAPE
+    t.mode, t.L = 1, -1
+    assert lib.attamba_chunk_attn_fwd(C.byref(t), None) == B.ERR_BAD_SHAPE
+    t.L = 0
+    assert lib.attamba_chunk_attn_fwd(C.byref(t), None) == B.ERR_NULL_ARG
+
+    assert lib.attamba_chunk_boundaries(None, 1, 4, 4, 0, 1, None, None, None, None) == B.ERR_NULL_ARG
+    assert lib.attamba_chunk_index(None, 1, 4, None, None, None) == B.ERR_NULL_ARG
+
+    c = B.DecodeCacheStruct()
+    c.B, c.H, c.hd, c.d, c.N, c.P, c.L, c.cap, c.dtype = 1, 2, 64, 128, 16, 4, 8, 4, 1
+    n = C.c_size_t()
+    assert lib.attamba_decode_workspace_size(C.byref(c), C.byref(n)) == 0 and n.value > 0
+    i = B.DecodeInputsStruct()
+    assert lib.attamba_decode_step(C.byref(c), C.byref(i), None) == B.ERR_NULL_ARG
+    c.d = 100
+    assert lib.attamba_decode_step(C.byref(c), C.byref(i), None) == B.ERR_BAD_SHAPE
+    c.d, c.hd, c.H = 96, 48, 2
+    assert lib.attamba_decode_step(C.byref(c), C.byref(i), None) == B.ERR_UNSUPPORTED

@@ -1,0 +1,299 @@
+"""GPU parity: every call of libattamba against the CPU oracle on the same seeded inputs.
+
+Bars: chunk layout bit-exact; float32 outputs within 1e-4 relative (+1e-5 absolute for values
+near zero); bf16 outputs within 2e-2 absolute + 2e-2 relative. Small cases are compared
+element by element; the full-size workloads on sampled chunks and query rows.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssm_compressed_chunked_amd as att
+from ssm_compressed_chunked_amd.pipeline import chunk_layout, prefill_forward
+from workloads import (PREFILL_BF16, TINY_FP32, TRAIN_BF16, VARCHUNK_BF16, make_prefill,
+                       make_ragged_prefill)
+
+pytestmark = pytest.mark.gpu
+
+MODE = {"train": att.MASK_TRAIN, "test": att.MASK_TEST}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_close(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if dtype == "fp32":
+        bound = 1e-4 * np.abs(ref) + 1e-5
+    else:
+        bound = 2e-2 + 2e-2 * np.abs(ref)
+    err = np.abs(got - ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; max err "
+                           f"{err.max():.3e} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+    return float(err.max())
+
+
+def to_dev(inp):
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    par = {k: v.cuda() for k, v in inp.param.items()}
+    return act, par
+
+
+def f64_inputs(inp):
+    names = list(inp.act) + list(inp.param)
+    return {k: inp.f64(k) for k in names}
+
+
+# ---------------------------------------------------------------------------------- layout
+@pytest.mark.parametrize("seq_lens,P,layer", [
+    ([256], 4, 0), ([2048] * 4, 8, 3), ([8192] * 2, 8, 0), ([5, 0, 12, 1, 33], 4, 1),
+    ([1, 1, 1], 3, 2), ([100], 1, 0), ([7, 64, 3], 64, 5), ([3000] * 3 + [1], 128, 130)])
+def test_uniform_boundaries_bit_exact(seq_lens, P, layer):
+    say(f"boundaries lens={seq_lens[:4]} P={P} layer={layer}")
+    seq_cu_h = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int32)
+    T = int(seq_cu_h[-1])
+    lay = chunk_layout(seq_cu_h, torch.from_numpy(seq_cu_h).cuda(), T, P, layer)
+    ref_cu, ref_tc, ref_ie = oracle.segment(seq_cu_h, P, layer)
+    assert lay.n_chunks == len(ref_cu) - 1
+    np.testing.assert_array_equal(lay.chunk_cu.cpu().numpy(), ref_cu)
+    np.testing.assert_array_equal(lay.token_chunk.cpu().numpy(), ref_tc)
+    np.testing.assert_array_equal(lay.is_end.cpu().numpy(), ref_ie)
+
+
+def test_many_sequences_boundaries():
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 40, size=3000)
+    seq_cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(seq_cu_h[-1])
+    lay = chunk_layout(seq_cu_h, torch.from_numpy(seq_cu_h).cuda(), T, 6, 4)
+    ref_cu, ref_tc, ref_ie = oracle.segment(seq_cu_h, 6, 4)
+    np.testing.assert_array_equal(lay.chunk_cu.cpu().numpy(), ref_cu)
+    np.testing.assert_array_equal(lay.token_chunk.cpu().numpy(), ref_tc)
+    np.testing.assert_array_equal(lay.is_end.cpu().numpy(), ref_ie)
+
+
+def test_random_chunk_index_bit_exact():
+    inp = make_prefill(VARCHUNK_BF16)
+    T = VARCHUNK_BF16.T
+    lay = chunk_layout(inp.seq_cu, torch.from_numpy(inp.seq_cu).cuda(), T, None, 0,
+                       chunk_lens=inp.chunk_lens)
+    ref_cu, ref_tc, ref_ie = oracle.segment(inp.seq_cu, chunk_lens=inp.chunk_lens)
+    assert lay.n_chunks == len(ref_cu) - 1 == 1855
+    np.testing.assert_array_equal(lay.chunk_cu.cpu().numpy(), ref_cu)
+    np.testing.assert_array_equal(lay.token_chunk.cpu().numpy(), ref_tc)
+    np.testing.assert_array_equal(lay.is_end.cpu().numpy(), ref_ie)
+
+
+# ------------------------------------------------------------------------- whole forward
+SMALL_CASES = [
+    # (name, base config, overrides, sequence lengths or None, random chunks)
+    ("tiny_fp32", TINY_FP32, {}, None, False),
+    ("tiny_fp32_ragged_test_L3", TINY_FP32, dict(mode="test", L=3, layer_idx=2), [70, 1, 130], False),
+    ("bf16_train_L64_o3", TRAIN_BF16, dict(B=2, n=300, d=256, H=4), None, False),
+    ("bf16_test_L64", PREFILL_BF16, dict(B=2, n=333, d=256, H=4), None, False),
+    ("bf16_test_L0", PREFILL_BF16, dict(B=1, n=200, d=128, H=2, L=0), None, False),
+    ("bf16_train_L0_P4", PREFILL_BF16, dict(B=1, n=257, d=128, H=2, L=0, P=4, mode="train"), None, False),
+    ("bf16_test_L1_ragged", PREFILL_BF16, dict(d=128, H=2, L=1, P=5, layer_idx=7), [1, 190, 0, 67], False),
+    ("bf16_random_chunks", VARCHUNK_BF16, dict(d=128, H=2), [150, 211], True),
+    ("bf16_hd128", PREFILL_BF16, dict(B=1, n=260, d=256, H=2, hd=128), None, False),
+    ("bf16_hd32_N32", PREFILL_BF16, dict(B=1, n=150, d=128, H=4, hd=32, N=32, mode="train", L=5), None, False),
+    ("fp32_hd64_train", TINY_FP32, dict(d=128, H=2, hd=64, n=190, P=3, L=7, layer_idx=1), None, False),
+]
+
+
+def _build_inputs(base, over, lens, rnd, seed=11):
+    cfg = base.with_(**over)
+    if lens is None:
+        inp = make_prefill(cfg, seed=seed) if not rnd else make_prefill(cfg.with_(chunking="random"), seed=seed)
+        return cfg, inp
+    chunk_lens = None
+    if rnd:
+        from workloads import draw_chunk_lengths
+        crng = np.random.default_rng(seed)
+        chunk_lens = []
+        for n in lens:
+            chunk_lens += draw_chunk_lengths(crng, n, cfg.chunk_len_lo, cfg.chunk_len_hi)
+    inp = make_ragged_prefill(cfg, lens, seed=seed, chunk_lens=chunk_lens)
+    return inp.cfg, inp
+
+
+@pytest.mark.parametrize("name,base,over,lens,rnd", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_forward_small_elementwise(name, base, over, lens, rnd):
+    cfg, inp = _build_inputs(base, over, lens, rnd)
+    say(f"forward {name}: T={int(inp.seq_cu[-1])} d={cfg.d} H={cfg.H} hd={cfg.hd} N={cfg.N} "
+        f"P={cfg.P} L={cfg.L} layer={cfg.layer_idx} mode={cfg.mode} random={rnd}")
+    act, par = to_dev(inp)
+    P = None if rnd else cfg.P
+    res = prefill_forward(act, par, inp.seq_cu, cfg.H, cfg.hd, P, cfg.layer_idx, cfg.L,
+                          MODE[cfg.mode], chunk_lens=inp.chunk_lens)
+    torch.cuda.synchronize()
+    ref = oracle.kvssm_forward(f64_inputs(inp), inp.seq_cu, cfg.H, cfg.hd, P, cfg.layer_idx,
+                               cfg.L, cfg.mode, chunk_lens=inp.chunk_lens)
+    T = int(inp.seq_cu[-1])
+    np.testing.assert_array_equal(res["layout"].chunk_cu.cpu().numpy(), ref["chunk_cu"])
+    for key in ("y_k", "y_v"):
+        check_close(res["scan"][key].float().cpu().numpy(), ref[key], cfg.dtype, key)
+    n = res["layout"].n_chunks
+    check_close(res["scan"]["kb"].float().cpu().numpy().reshape(n, cfg.H, cfg.hd), ref["kb"],
+                cfg.dtype, "kb")
+    check_close(res["scan"]["vb"].float().cpu().numpy().reshape(n, cfg.H, cfg.hd), ref["vb"],
+                cfg.dtype, "vb")
+    check_close(res["out"].float().cpu().numpy(), ref["out"], cfg.dtype, "out")
+    lse = res["lse"].cpu().numpy()
+    fin = np.isfinite(ref["lse"])
+    assert (np.isfinite(lse) == fin).all()
+    check_close(lse[fin], ref["lse"][fin], cfg.dtype, "lse")
+
+
+def test_h_last_handoff():
+    cfg = TRAIN_BF16.with_(d=128, H=2, n=75, B=3)
+    inp = make_ragged_prefill(cfg, [75, 9, 40], seed=3)
+    act, par = to_dev(inp)
+    seq_cu = torch.from_numpy(inp.seq_cu).cuda()
+    T = int(inp.seq_cu[-1])
+    lay = chunk_layout(inp.seq_cu, seq_cu, T, cfg.P, cfg.layer_idx)
+    s = att.kvssm_scan(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"], act["bm_v"],
+                       act["cm_v"], par["A_k"], par["A_v"], par["D_k"], par["D_v"], par["bias_k"],
+                       par["bias_v"], lay.chunk_cu, seq_cu=seq_cu, h_last=True)
+    torch.cuda.synchronize()
+    f = f64_inputs(inp)
+    ends = set(int(v) - 1 for v in inp.seq_cu[1:])
+    for tag in ("k", "v"):
+        _, snaps = oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
+                                         f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"],
+                                         oracle.segment(inp.seq_cu, cfg.P, cfg.layer_idx)[0],
+                                         snapshot_after=ends)
+        got = s[f"h_last_{tag}"].cpu().numpy()
+        for si, e in enumerate(sorted(ends)):
+            # the state itself is float32 on the GPU: 1e-3 relative to the state scale
+            ref = snaps[e]
+            assert np.abs(got[si] - ref).max() <= 1e-3 * (np.abs(ref).max() + 1e-6)
+
+
+# ------------------------------------------------------- full-size workloads, sampled checks
+@pytest.mark.parametrize("cfg", [TRAIN_BF16, PREFILL_BF16, VARCHUNK_BF16], ids=lambda c: c.name)
+def test_full_size_sampled(cfg):
+    say(f"full-size {cfg.name}")
+    inp = make_prefill(cfg)
+    act, par = to_dev(inp)
+    rnd = cfg.chunking == "random"
+    P = None if rnd else cfg.P
+    res = prefill_forward(act, par, inp.seq_cu, cfg.H, cfg.hd, P, cfg.layer_idx, cfg.L,
+                          MODE[cfg.mode], chunk_lens=inp.chunk_lens)
+    torch.cuda.synchronize()
+    ref_cu, ref_tc, ref_ie = oracle.segment(inp.seq_cu, P, cfg.layer_idx, inp.chunk_lens)
+    np.testing.assert_array_equal(res["layout"].chunk_cu.cpu().numpy(), ref_cu)
+    np.testing.assert_array_equal(res["layout"].token_chunk.cpu().numpy(), ref_tc)
+    f = f64_inputs(inp)
+    T, n = cfg.T, len(ref_cu) - 1
+    rng = np.random.default_rng(0)
+    # scan: sampled chunks (the state restarts at every chunk, so each is checked on its own)
+    for q in sorted(set(rng.integers(0, n, 6).tolist()) | {0, n - 1}):
+        a, b = int(ref_cu[q]), int(ref_cu[q + 1])
+        for tag in ("k", "v"):
+            y, _ = oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
+                                         f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"], ref_cu,
+                                         t_begin=a, t_end=b)
+            check_close(res["scan"][f"y_{tag}"][a:b].float().cpu().numpy(), y, cfg.dtype,
+                        f"y_{tag} chunk {q}")
+    # attention: sampled rows of every sequence, against the oracle over its own K/V
+    seq0 = int(inp.seq_cu[0]), int(inp.seq_cu[1])
+    a, b = seq0
+    yk, _ = oracle.selective_scan(f["x"], f["dt_k"], f["bias_k"], f["A_k"], f["bm_k"], f["cm_k"],
+                                  f["D_k"], ref_cu, t_begin=a, t_end=b)
+    yv, _ = oracle.selective_scan(f["x"], f["dt_v"], f["bias_v"], f["A_v"], f["bm_v"], f["cm_v"],
+                                  f["D_v"], ref_cu, t_begin=a, t_end=b)
+    rows = np.unique(np.concatenate([rng.integers(a, b, 40), [a, a + 1, b - 1, b - 2]]))
+    H, hd = cfg.H, cfg.hd
+    k3 = np.zeros((T, H, hd)); v3 = np.zeros((T, H, hd))
+    k3[a:b] = yk.reshape(-1, H, hd); v3[a:b] = yv.reshape(-1, H, hd)
+    out, lse = oracle.chunk_attention(f["q"].reshape(T, H, hd), k3, v3, inp.seq_cu, ref_tc, ref_ie,
+                                      cfg.L, cfg.mode, rows=rows)
+    check_close(res["out"][rows].float().cpu().numpy(), out, cfg.dtype, "out rows")
+    check_close(res["lse"][:, rows].cpu().numpy(), lse, cfg.dtype, "lse rows")
+
+
+# ------------------------------------------------------------------------------ decode
+@pytest.mark.parametrize("H,hd,N,P,L,layer,n0,steps,dtype", [
+    (2, 128, 16, 4, 8, 0, 21, 13, "bf16"),
+    (4, 64, 16, 4, 5, 1, 9, 11, "bf16"),
+    (2, 32, 32, 3, 1, 2, 7, 9, "bf16"),
+    (2, 64, 16, 4, 0, 0, 12, 10, "bf16"),
+    (2, 32, 16, 2, 600, 1, 300, 8, "bf16"),
+    (2, 32, 16, 4, 6, 3, 17, 9, "fp32"),
+])
+def test_decode_matches_prefill_rows(H, hd, N, P, L, layer, n0, steps, dtype):
+    say(f"decode H={H} hd={hd} N={N} P={P} L={L} layer={layer} n0={n0} dtype={dtype}")
+    B = 3
+    d = H * hd
+    o = layer % P
+    n_total = n0 + steps
+    n_total += (o - n_total) % P
+    base = PREFILL_BF16 if dtype == "bf16" else TINY_FP32
+    cfg = base.with_(B=B, n=n_total, d=d, H=H, hd=hd, N=N, P=P, L=L, layer_idx=layer, mode="test")
+    inp = make_prefill(cfg, seed=100 + n0)
+    f = f64_inputs(inp)
+    T = cfg.T
+    ref = oracle.kvssm_forward(f, inp.seq_cu, H, hd, P, layer, L, "test")
+    chunk_cu = ref["chunk_cu"]
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    cap = n_total // P + 4
+    n_bound0 = sum(1 for j in range(n0) if oracle.is_chunk_end_at(j, P, layer))
+    cache = att.DecodeCache(B, H, hd, N, P, L, layer, cap, tdt, inp.param, pos=n0, n_bound=n_bound0)
+    for b in range(B):
+        a = int(inp.seq_cu[b])
+        snaps = {}
+        for tag in ("k", "v"):
+            _, sn = oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
+                                          f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"], chunk_cu,
+                                          t_begin=a, t_end=a + n0, snapshot_after={a + n0 - 1})
+            snaps[tag] = sn[a + n0 - 1]
+        st = oracle.decode_state_from_prefix(ref["y_k"][a:a + n0], ref["y_v"][a:a + n0],
+                                             snaps["k"], snaps["v"], n0, H, hd, P, layer, L)
+        for idx, (_, kr, vr) in enumerate(st.bounds):
+            cache.kb[b, :, idx] = torch.from_numpy(kr).to(tdt)
+            cache.vb[b, :, idx] = torch.from_numpy(vr).to(tdt)
+        for (pos, kr, vr) in st.recent:
+            cache.kw[b, :, pos % L] = torch.from_numpy(kr).to(tdt)
+            cache.vw[b, :, pos % L] = torch.from_numpy(vr).to(tdt)
+        cache.h_k[b] = torch.from_numpy(st.h_k).float()
+        cache.h_v[b] = torch.from_numpy(st.h_v).float()
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    for i in range(n0, n_total):
+        rows = torch.from_numpy(inp.seq_cu[:-1] + i).long().cuda()
+        out = att.decode_step(cache, act["q"][rows].view(B, H, hd).contiguous(),
+                              act["x"][rows].contiguous(), act["dt_k"][rows].contiguous(),
+                              act["dt_v"][rows].contiguous(), act["bm_k"][rows].contiguous(),
+                              act["cm_k"][rows].contiguous(), act["bm_v"][rows].contiguous(),
+                              act["cm_v"][rows].contiguous())
+        torch.cuda.synchronize()
+        check_close(out.float().cpu().numpy(), ref["out"][inp.seq_cu[:-1] + i], dtype, f"decode pos {i}")
+    assert cache.pos == n_total
+    assert cache.n_bound == sum(1 for j in range(n_total) if oracle.is_chunk_end_at(j, P, layer))
+
+
+def test_decode_rejects_full_cache_and_bad_mirror():
+    B, H, hd, N, P, L = 1, 2, 32, 16, 4, 4
+    par = make_prefill(TINY_FP32.with_(d=64, H=H, hd=hd)).param
+    cache = att.DecodeCache(B, H, hd, N, P, L, 0, 1, torch.bfloat16, par, pos=3, n_bound=0)
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device="cuda")
+    args = (z(B, H, hd), z(B, H * hd), z(B, H * hd), z(B, H * hd), z(B, N), z(B, N), z(B, N), z(B, N))
+    att.decode_step(cache, *args)              # pos 3 ends a chunk: appended at slot 0
+    assert cache.n_bound == 1
+    cache.set_position(7, 1)                   # pos 7 ends the next chunk: cache full
+    with pytest.raises(att.AttambaError) as e:
+        att.decode_step(cache, *args)
+    assert e.value.status == 4
+    cache.set_position(8, 1)                   # two ends (3, 7) precede pos 8, not one
+    with pytest.raises(att.AttambaError) as e:
+        att.decode_step(cache, *args)
+    assert e.value.status == 2
