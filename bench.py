@@ -1,0 +1,352 @@
+"""Throughput of the Attamba KV-SSM forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input already resident
+in HBM: chunk segmentation, the fused SSM_K/SSM_V scan, and the chunk-aware attention. The
+default workload is the prefill configuration (bf16, B=2, n=8192, d=2048, 32 heads x 64,
+N=16, P=8, L=64, uniform chunks, M_test + window). Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload prefill_bf16|varchunk_bf16|train_bf16]
+    python bench.py --workload decode_bf16      # decode configuration, separate line
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec fwd (KV-SSM scan+chunk attn); scan HBM GB/s %peak; attn MFMA %"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+# VALU issue capacity: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-instruction slots per second.
+VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+# Minimal VALU issue slots per state update of the scan: multiply for the exponent, v_exp_f32
+# (half rate on gfx950: 2 slots), multiply for the input term, FMA state, FMA output.
+SLOTS_PER_UPDATE = 6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "ssm_compressed_chunked_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, sources) -> dict | None:
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(*sources):
+        return None
+    return rec
+
+
+def scan_algorithmic_bytes(cfg) -> int:
+    """x once, dt_K, dt_V, Bm/Cm of both SSMs, y_K and y_V (parameters and the boundary copy
+    excluded): 2 * (5 d + 4 N) bytes per token at bf16."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    return cfg.T * e * (5 * cfg.d + 4 * cfg.N)
+
+
+def attention_pairs(seq_cu, chunk_cu_np, token_chunk_np, L, train) -> int:
+    """Visible (query, key) pairs per head: for every row, (i - w_i + 1) band keys plus the
+    E_i boundary states of chunks that end before w_i."""
+    total = 0
+    for s in range(len(seq_cu) - 1):
+        s0, s1 = int(seq_cu[s]), int(seq_cu[s + 1])
+        if s1 <= s0:
+            continue
+        i = np.arange(s0, s1)
+        w = np.maximum(s0, i - L + 1)
+        if train:
+            w = np.minimum(w, chunk_cu_np[token_chunk_np[i]])
+        c0 = token_chunk_np[s0]
+        wi = np.minimum(w, s1 - 1)
+        E = np.where(w < s1, token_chunk_np[wi] - c0, token_chunk_np[s1 - 1] + 1 - c0)
+        total += int(((i - w + 1) + E).sum())
+    return total
+
+
+def cpu_baseline(cfg, inp, T_full):
+    """The oracle as it stands, on a bounded sample of the same workload: the scan over the
+    first 1024 tokens of sequence 0 (all channels, both SSMs) and the attention of (sequence
+    0, head 0) over all its rows; scaled to the whole batch (scan is linear in tokens,
+    attention in sequence-head pairs)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    f = {k: inp.f64(k) for k in list(inp.act) + list(inp.param)}
+    chunk_cu, tc, ie = oracle.segment(inp.seq_cu, None if inp.chunk_lens is not None else cfg.P,
+                                      cfg.layer_idx, inp.chunk_lens)
+    n_scan = min(1024, int(inp.seq_cu[1]))
+    n_scan = int(chunk_cu[np.searchsorted(chunk_cu, n_scan)])   # whole chunks
+    t0 = time.perf_counter()
+    for tag in ("k", "v"):
+        oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
+                              f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"], chunk_cu,
+                              t_begin=0, t_end=n_scan)
+    t_scan = time.perf_counter() - t0
+    s0, s1 = int(inp.seq_cu[0]), int(inp.seq_cu[1])
+    H, hd = cfg.H, cfg.hd
+    q = f["q"][s0:s1].reshape(-1, H, hd)[:, :1]
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((s1 - s0, 1, hd))
+    v = rng.standard_normal((s1 - s0, 1, hd))
+    t0 = time.perf_counter()
+    oracle.chunk_attention(q, k, v, [0, s1 - s0], tc[s0:s1] - tc[s0], ie[s0:s1], cfg.L, cfg.mode)
+    t_attn = time.perf_counter() - t0
+    n_pairs = (len(inp.seq_cu) - 1) * H
+    est = t_scan * (T_full / n_scan) + t_attn * n_pairs
+    return {"value": T_full / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle scan of tokens 0..{n_scan - 1} of sequence 0 (all {cfg.d} channels, "
+                       f"both SSMs: {t_scan:.2f} s) scaled by {T_full / n_scan:.1f}; oracle attention of "
+                       f"sequence 0, head 0 ({s1 - s0} rows: {t_attn:.2f} s) scaled by {n_pairs} "
+                       f"sequence-head pairs; estimated {est:.1f} s per step")}
+
+
+def bench_prefill(args):
+    import torch
+    import ssm_compressed_chunked_amd as att
+    from ssm_compressed_chunked_amd import _binding as Bd
+    from ssm_compressed_chunked_amd.pipeline import chunk_layout
+    from workloads import PREFILL_CONFIGS, make_prefill
+
+    cfg = PREFILL_CONFIGS[args.workload]
+    inp = make_prefill(cfg)
+    dev = torch.device("cuda", 0)
+    act = {k: v.to(dev) for k, v in inp.act.items()}
+    par = {k: v.to(dev) for k, v in inp.param.items()}
+    seq_cu = torch.from_numpy(inp.seq_cu).to(dev)
+    T, d, H, hd = cfg.T, cfg.d, cfg.H, cfg.hd
+    rnd = cfg.chunking == "random"
+    P = None if rnd else cfg.P
+    mode = att.MASK_TRAIN if cfg.mode == "train" else att.MASK_TEST
+    max_len = int(np.max(np.diff(inp.seq_cu)))
+    # outputs allocated once (the library never allocates)
+    lay0 = chunk_layout(inp.seq_cu, seq_cu, T, P, cfg.layer_idx, inp.chunk_lens)
+    n = lay0.n_chunks
+    chunk_cu_host = None if not rnd else att.chunk_cu_from_lengths(inp.seq_cu, inp.chunk_lens)
+    chunk_cu = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    if rnd:
+        chunk_cu.copy_(torch.from_numpy(chunk_cu_host))
+    token_chunk = torch.empty(T, dtype=torch.int32, device=dev)
+    is_end = torch.empty(T, dtype=torch.uint8, device=dev)
+    y_k = torch.empty_like(act["x"])
+    y_v = torch.empty_like(act["x"])
+    kb = torch.empty((n, d), dtype=act["x"].dtype, device=dev)
+    vb = torch.empty((n, d), dtype=act["x"].dtype, device=dev)
+    out = torch.empty((T, H, hd), dtype=act["x"].dtype, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if rnd:
+            att.chunk_index(chunk_cu, T, token_chunk, is_end, stream=stream)
+        else:
+            att.chunk_boundaries(seq_cu, T, cfg.P, cfg.layer_idx, n, chunk_cu, token_chunk,
+                                 is_end, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        att.kvssm_scan(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"], act["bm_v"],
+                       act["cm_v"], par["A_k"], par["A_v"], par["D_k"], par["D_v"], par["bias_k"],
+                       par["bias_v"], chunk_cu, y_k=y_k, y_v=y_v, kb=kb, vb=vb, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        att.chunk_attn_fwd(act["q"].view(T, H, hd), y_k.view(T, H, hd), y_v.view(T, H, hd),
+                           kb.view(n, H, hd), vb.view(n, H, hd), seq_cu, chunk_cu, token_chunk,
+                           max_len, cfg.L, mode, out=out, lse=lse, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-job timing: exactly K steps, synchronised on both sides
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel durations with HIP events on the launch stream (separate pass, same work)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    seg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    ms = wall * 1e3 / args.steps
+    tok_s = T / (wall / args.steps)
+    pairs = attention_pairs(inp.seq_cu, lay0.chunk_cu.cpu().numpy(), lay0.token_chunk.cpu().numpy(),
+                            cfg.L, mode == att.MASK_TRAIN)
+    attn_flop = 4.0 * hd * H * pairs
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    scan_bytes = scan_algorithmic_bytes(cfg)
+    scan_gbps = scan_bytes / (scan_ms * 1e-3) / 1e9
+    updates = 2 * T * d * cfg.N
+    scan_slots = SLOTS_PER_UPDATE * updates
+    scan_alu_tslots = scan_slots / (scan_ms * 1e-3) / 1e12
+    alu_peak = VALU_SLOTS_PER_S / 1e12
+    traffic = measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"])
+    roofline = {"bound": "alu", "kernel": "kvssm_scan_kernel", "achieved": round(scan_alu_tslots, 3),
+                "peak": round(alu_peak, 3), "unit": "T VALU-slot/s", "frac": round(scan_alu_tslots / alu_peak, 4),
+                "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                "work_per_launch": f"{updates} state updates x {SLOTS_PER_UPDATE} slots",
+                "avg_launch_us": round(scan_ms * 1e3, 2)}
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02^2), projections computed)",
+        "config": {"workload": cfg.name, "B": cfg.B, "n": cfg.n, "d_model": d, "heads": H,
+                   "head_dim": hd, "N": cfg.N, "P": cfg.P, "L": cfg.L, "layer_idx": cfg.layer_idx,
+                   "mask": "M_train+window" if mode == att.MASK_TRAIN else "M_test+window",
+                   "chunking": cfg.chunking, "n_chunks": n},
+        "roofline": roofline,
+        "kernels_us": {"segmentation": round(seg_ms * 1e3, 2), "kvssm_scan": round(scan_ms * 1e3, 2),
+                       "chunk_attn": round(attn_ms * 1e3, 2)},
+        "scan_hbm": {"algorithmic_bytes": scan_bytes, "GBps": round(scan_gbps, 1),
+                     "frac_of_8TBps": round(scan_gbps / HBM_PEAK_GBPS, 4)},
+        "attn_mfma": {"algorithmic_flop": attn_flop, "visible_pairs_per_head": pairs,
+                      "TFLOPs": round(attn_tflops, 2),
+                      "frac_of_2.5PF": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, T)
+    print(json.dumps(line), flush=True)
+
+
+def bench_decode(args):
+    import torch
+    import ssm_compressed_chunked_amd as att
+    from workloads import DECODE_CONFIGS, make_decode
+
+    cfg = DECODE_CONFIGS[args.workload]
+    n_bound = att.count_chunks([0, cfg.ctx], cfg.P, cfg.layer_idx)
+    o = cfg.layer_idx % cfg.P
+    if (cfg.ctx - o) % cfg.P != 0:
+        raise SystemExit("decode bench expects a context that ends on a chunk boundary")
+    steps = min(args.steps, cfg.steps)
+    inp = make_decode(cfg, n_bound=n_bound, steps=cfg.steps, device="cuda")
+    dtype = inp.kb.dtype
+    cap = n_bound + cfg.steps // cfg.P + 2
+    cache = att.DecodeCache(cfg.B, cfg.H, cfg.hd, cfg.N, cfg.P, cfg.L, cfg.layer_idx, cap, dtype,
+                            inp.param, pos=cfg.ctx, n_bound=n_bound)
+    cache.kb[:, :, :n_bound] = inp.kb
+    cache.vb[:, :, :n_bound] = inp.vb
+    cache.kw.copy_(inp.kw)
+    cache.vw.copy_(inp.vw)
+    del inp.kb, inp.vb
+    a = {k: v.cuda() for k, v in inp.act.items()}
+    out = torch.empty((cfg.B, cfg.H, cfg.hd), dtype=dtype, device="cuda")
+
+    def run(n_steps):
+        for s in range(n_steps):
+            att.decode_step(cache, a["q"][s].view(cfg.B, cfg.H, cfg.hd), a["x"][s], a["dt_k"][s],
+                            a["dt_v"][s], a["bm_k"][s], a["cm_k"][s], a["bm_v"][s], a["cm_v"][s], out=out)
+
+    run(min(args.warmup, cfg.steps))
+    torch.cuda.synchronize()
+    cache.set_position(cfg.ctx, n_bound)
+    t0 = time.perf_counter()
+    run(cfg.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    keys = 0
+    for s in range(cfg.steps):
+        pos = cfg.ctx + s
+        w = max(0, pos - cfg.L + 1)
+        keys += att_ends_before(w, cfg.P, o) + (pos - w + 1)
+    e = 2 if cfg.dtype == "bf16" else 4
+    kv_bytes = keys * cfg.B * cfg.H * cfg.hd * 2 * e
+    state_bytes = cfg.steps * 2 * 2 * cfg.B * cfg.d * cfg.N * 4
+    gbps = (kv_bytes + state_bytes) / wall / 1e9
+    line = {"metric": "decode tokens/s (boundary-state cache)", "value": round(cfg.B * cfg.steps / wall, 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": cfg.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall * 1e3 / cfg.steps, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+            "config": {"workload": cfg.name, "B": cfg.B, "ctx": cfg.ctx, "d_model": cfg.d,
+                       "heads": cfg.H, "head_dim": cfg.hd, "N": cfg.N, "P": cfg.P, "L": cfg.L},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
+    print(json.dumps(line), flush=True)
+
+
+def bench_copy(args):
+    """A plain device copy of 512 MiB: the reference point that scales rocprofv3's FETCH_SIZE
+    and WRITE_SIZE counters to bytes (the copy moves exactly 512 MiB each way per launch)."""
+    import torch
+    nbytes = 512 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gbps = 2 * nbytes * args.steps / wall / 1e9
+    print(json.dumps({"metric": "device copy", "bytes_each_way": nbytes, "steps": args.steps,
+                      "GBps_read_plus_write": round(gbps, 1)}), flush=True)
+
+
+def att_ends_before(x, P, o):
+    if x <= 0:
+        return 0
+    if o == 0:
+        return x // P
+    return (x - o) // P + 1 if x >= o else 0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by batch, head or sequence with no exchange beyond one "
+              "all-gather of boundary states; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    if args.workload == "copy":
+        bench_copy(args)
+    elif args.workload.startswith("decode"):
+        bench_decode(args)
+    else:
+        bench_prefill(args)
+
+
+if __name__ == "__main__":
+    main()

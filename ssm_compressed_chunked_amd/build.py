@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattamba.so")
-SOURCES = ["boundaries.hip", "kvssm_scan.hip", "chunk_attn.hip", "decode.hip",
+SOURCES = ["boundaries.hip", "kvssm_scan.hip", "chunk_attn.hip", "attn_mfma.hip", "decode.hip",
            "abi.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -103,8 +103,7 @@ hipError_t launch_chunk_attn(const attamba_attn_args& a, float scale, hipStream_
   p.seq_cu = a.seq_cu; p.chunk_cu = a.chunk_cu; p.token_chunk = a.token_chunk;
   p.out = a.out; p.lse = a.lse;
   if (a.dtype == ATTAMBA_BF16) {
-    if (a.hd == 64) return launch_rowwise<__bf16, 64>(p, stream);
-    if (a.hd == 128) return launch_rowwise<__bf16, 128>(p, stream);
+    if (a.hd == 64 || a.hd == 128) return launch_attn_mfma(p, a.hd, stream);
     return launch_rowwise<__bf16, 32>(p, stream);
   }
   if (a.hd == 32) return launch_rowwise<float, 32>(p, stream);

@@ -20,6 +20,9 @@ struct AttnParams {
   float* lse;
 };
 
+// bf16 matrix-core attention for hd 64 and 128.
+hipError_t launch_attn_mfma(const AttnParams& p, int hd, hipStream_t stream);
+
 hipError_t launch_kvssm_scan(const attamba_scan_args& a, hipStream_t stream);
 hipError_t launch_chunk_attn(const attamba_attn_args& a, float scale, hipStream_t stream);
 
