@@ -183,7 +183,8 @@ typedef struct {
 } attamba_attn_args;
 
 /* Errors: NULL_ARG, BAD_SHAPE (negative sizes, S < 1, max_seqlen < 1 with T > 0,
- * L < 0, unknown mode), BAD_DTYPE, UNSUPPORTED (hd not 32/64/128), HIP. */
+ * L < 0, unknown mode), BAD_DTYPE, UNSUPPORTED (hd not 32/64/128, or T*H*hd of 2^31 elements
+ * or more), HIP. */
 int attamba_chunk_attn_fwd(const attamba_attn_args* args, attamba_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------

@@ -29,6 +29,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
          "-I", os.path.join(ROOT, "include")]
 
 
+# Matrix-core accumulators in VGPRs (not AGPRs) so the softmax rescale of the output
+# accumulator needs no AGPR<->VGPR copies.
+EXTRA = {"attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
@@ -48,7 +53,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        return _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        return _run([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         logs = list(ex.map(compile_one, zip(SOURCES, objs)))

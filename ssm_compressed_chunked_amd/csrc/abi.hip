@@ -172,6 +172,8 @@ int attamba_chunk_attn_fwd(const attamba_attn_args* a, attamba_stream_t stream) 
                 a->H, a->S, a->max_seqlen, a->n_chunks, a->L, a->mode);
   if (a->hd != 32 && a->hd != 64 && a->hd != 128)
     return fail(ATTAMBA_ERR_UNSUPPORTED, "chunk_attn_fwd: hd=%d (32, 64 or 128)", a->hd);
+  if (static_cast<int64_t>(a->T) * a->H * a->hd > INT32_MAX)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "chunk_attn_fwd: T*H*hd exceeds 2^31 elements");
   if (a->T > 0 && (!a->q || !a->k || !a->v || !a->kb || !a->vb || !a->seq_cu || !a->chunk_cu ||
                    !a->token_chunk || !a->out))
     return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_fwd: a required pointer is null");

@@ -20,6 +20,8 @@
 // division are per-lane operations; the P operand of the second product is the first
 // product's accumulator converted to bf16 in place (the keys are taken in the accumulator's
 // row order, and V^T is read in the same order).
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -68,6 +70,55 @@ struct TileRegs {
   uint4 v0[VU], v1[VU];
 };
 
+// Global -> registers for one tile of keys base .. base + BN - 1. Keys past `top` (the last
+// valid key) re-read row `top` instead of branching around the load: every row that could
+// see such a key masks it. Offsets are 32-bit (element counts below 2^31, checked at the ABI).
+template <int HD>
+__device__ __forceinline__ void tile_load(TileRegs<HD>& r, const __bf16* __restrict__ kp,
+                                          const __bf16* __restrict__ vp, int base, int top,
+                                          int hs, int tid) {
+#pragma unroll
+  for (int u = 0; u < TileRegs<HD>::KU; ++u) {
+    const int piece = tid + u * NT;
+    const int key = piece / (HD / 8), seg = piece % (HD / 8);
+    const int kk = min(base + key, top);
+    r.k[u] = *reinterpret_cast<const uint4*>(kp + (kk * hs + seg * 8));
+  }
+#pragma unroll
+  for (int u = 0; u < TileRegs<HD>::VU; ++u) {
+    const int unit = tid + u * NT;
+    const int gq = unit % (HD / 8), kp2 = unit / (HD / 8);
+    const int k0 = min(base + 2 * kp2, top), k1 = min(base + 2 * kp2 + 1, top);
+    r.v0[u] = *reinterpret_cast<const uint4*>(vp + (k0 * hs + gq * 8));
+    r.v1[u] = *reinterpret_cast<const uint4*>(vp + (k1 * hs + gq * 8));
+  }
+}
+
+// Registers -> LDS: K rows as they are; V transposed to [hd][key], two keys per 32-bit word.
+template <int HD>
+__device__ __forceinline__ void tile_store(const TileRegs<HD>& r, __bf16* sk, __bf16* sv, int tid) {
+  constexpr int KST = Smem<HD>::KST, VST = Smem<HD>::VST;
+#pragma unroll
+  for (int u = 0; u < TileRegs<HD>::KU; ++u) {
+    const int piece = tid + u * NT;
+    const int key = piece / (HD / 8), seg = piece % (HD / 8);
+    *reinterpret_cast<uint4*>(sk + key * KST + seg * 8) = r.k[u];
+  }
+#pragma unroll
+  for (int u = 0; u < TileRegs<HD>::VU; ++u) {
+    const int unit = tid + u * NT;
+    const int gq = unit % (HD / 8), kp2 = unit / (HD / 8);
+    const uint32_t a[4] = {r.v0[u].x, r.v0[u].y, r.v0[u].z, r.v0[u].w};
+    const uint32_t b[4] = {r.v1[u].x, r.v1[u].y, r.v1[u].z, r.v1[u].w};
+    uint32_t* dst = reinterpret_cast<uint32_t*>(sv + (gq * 8) * VST + 2 * kp2);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      dst[(2 * e2) * (VST / 2)] = (a[e2] & 0xffffu) | (b[e2] << 16);
+      dst[(2 * e2 + 1) * (VST / 2)] = (a[e2] >> 16) | (b[e2] & 0xffff0000u);
+    }
+  }
+}
+
 template <int HD>
 __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   constexpr int KST = Smem<HD>::KST, VST = Smem<HD>::VST;
@@ -75,9 +126,18 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   constexpr int OB = HD / 32;     // 32-row hd blocks of O^T
   __shared__ Smem<HD> sm;
 
-  const int s = blockIdx.z, h = blockIdx.y;
+  // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. All query tiles
+  // of one (sequence, head) are placed on one XCD, consecutively, so that its boundary-state
+  // prefix is fetched into that L2 once; within a (sequence, head) the tiles with the most
+  // keys (the last rows) are issued first so that light tiles form the tail of the grid.
+  const int n_qt = ceil_div(p.max_seqlen, BM);
+  const int id = blockIdx.x, slot = id >> 3;
+  const int bh = (slot / n_qt) * 8 + (id & 7);
+  if (bh >= p.S * p.H) return;
+  const int s = bh / p.H, h = bh % p.H;
+  const int qt = n_qt - 1 - slot % n_qt;
   const int s0 = p.seq_cu[s], s1 = p.seq_cu[s + 1];
-  const int r0 = s0 + blockIdx.x * BM;
+  const int r0 = s0 + qt * BM;
   if (r0 >= s1) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int q = lane & 31, hf = lane >> 5;
@@ -120,64 +180,26 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const __bf16* vbp = static_cast<const __bf16*>(p.vb) + h * HD;
   const __bf16* ktp = static_cast<const __bf16*>(p.k) + h * HD;
   const __bf16* vtp = static_cast<const __bf16*>(p.v) + h * HD;
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
-  // global -> registers for tile t (keys outside the tile's valid range read as zero)
-  auto load_tile = [&](int t, TileRegs<HD>& r) {
-    const bool bnd = t < nbt;
-    const int base = bnd ? c0 + t * BN : band0 + (t - nbt) * BN;
-    const int lim = bnd ? c0 + gl.E : last + 1;          // exclusive key limit
-    const __bf16* kp = bnd ? kbp : ktp;
-    const __bf16* vp = bnd ? vbp : vtp;
-#pragma unroll
-    for (int u = 0; u < TileRegs<HD>::KU; ++u) {
-      const int piece = tid + u * NT;                  // 16-byte piece of the K tile
-      const int key = piece / (HD / 8), seg = piece % (HD / 8);
-      const int kk = base + key;
-      r.k[u] = kk < lim ? *reinterpret_cast<const uint4*>(kp + kk * hs + seg * 8) : zero4;
-    }
-#pragma unroll
-    for (int u = 0; u < TileRegs<HD>::VU; ++u) {
-      const int unit = tid + u * NT;
-      const int gq = unit % (HD / 8), kp2 = unit / (HD / 8);
-      const int k0 = base + 2 * kp2;
-      r.v0[u] = k0 < lim ? *reinterpret_cast<const uint4*>(vp + k0 * hs + gq * 8) : zero4;
-      r.v1[u] = k0 + 1 < lim ? *reinterpret_cast<const uint4*>(vp + (k0 + 1) * hs + gq * 8) : zero4;
-    }
-  };
-  auto store_tile = [&](int buf, const TileRegs<HD>& r) {
-#pragma unroll
-    for (int u = 0; u < TileRegs<HD>::KU; ++u) {
-      const int piece = tid + u * NT;
-      const int key = piece / (HD / 8), seg = piece % (HD / 8);
-      *reinterpret_cast<uint4*>(&sm.k[buf][key * KST + seg * 8]) = r.k[u];
-    }
-#pragma unroll
-    for (int u = 0; u < TileRegs<HD>::VU; ++u) {
-      const int unit = tid + u * NT;
-      const int gq = unit % (HD / 8), kp2 = unit / (HD / 8);
-      const uint32_t a[4] = {r.v0[u].x, r.v0[u].y, r.v0[u].z, r.v0[u].w};
-      const uint32_t b[4] = {r.v1[u].x, r.v1[u].y, r.v1[u].z, r.v1[u].w};
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.v[buf][(gq * 8) * VST + 2 * kp2]);
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        dst[(2 * e2) * (VST / 2)] = (a[e2] & 0xffffu) | (b[e2] << 16);
-        dst[(2 * e2 + 1) * (VST / 2)] = (a[e2] >> 16) | (b[e2] & 0xffff0000u);
-      }
-    }
-  };
-
+  const int hs32 = p.H * HD;
+  const int topb = c0 + gl.E - 1;   // last boundary key of the workgroup
+  // tile t: boundary tiles first, then band tiles
+  auto src_k = [&](int t) { return t < nbt ? kbp : ktp; };
+  auto src_v = [&](int t) { return t < nbt ? vbp : vtp; };
+  auto base_of = [&](int t) { return t < nbt ? c0 + t * BN : band0 + (t - nbt) * BN; };
+  auto top_of = [&](int t) { return t < nbt ? topb : last; };
   TileRegs<HD> regs;
   if (ntiles > 0) {
-    load_tile(0, regs);
-    store_tile(0, regs);
+    tile_load<HD>(regs, src_k(0), src_v(0), base_of(0), top_of(0), hs32, tid);
+    tile_store<HD>(regs, sm.k[0], sm.v[0], tid);
   }
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1, regs);
+    const int tn = more ? t + 1 : t;
+    tile_load<HD>(regs, src_k(tn), src_v(tn), base_of(tn), top_of(tn), hs32, tid);
 
     // which rows of this wave see which keys of the tile
     const bool bnd = t < nbt;
@@ -193,33 +215,53 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
     if (!skip) {
       const __bf16* sk = sm.k[buf];
       const __bf16* sv = sm.v[buf];
+      bf16x8 ka[2][QS];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < QS; ++st)
+          ka[kb][st] = *reinterpret_cast<const bf16x8*>(sk + (32 * kb + q) * KST + 16 * st + 8 * hf);
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
 #pragma unroll
-        for (int st = 0; st < QS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (32 * kb + q) * KST + 16 * st + 8 * hf);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], sacc[kb], 0, 0, 0);
+        for (int st = 0; st < QS; ++st)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][st], qf[st], sacc[kb], 0, 0, 0);
+      }
+      // V^T fragments of this tile (read while the products above drain)
+      bf16x8 va[OB][4];
+#pragma unroll
+      for (int j = 0; j < OB; ++j) {
+        const __bf16* vrow = sv + (32 * j + q) * VST + 4 * hf;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * ks);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16 * ks + 8);
+          va[j][ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       }
       // accumulator row v of block kb is key 32 kb + 8 (v / 4) + 4 hf + v % 4
+      float sc[32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[16 * kb + v] = sacc[kb][v];
       if (!full) {
+        const int lo = bnd ? INT_MIN : g.w;
+        const int hi = bnd ? c0 + g.E - 1 : ic;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = base + 32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3);
-            const bool vis = bnd ? key < c0 + g.E : (key >= g.w && key <= ic);
-            if (!vis) sacc[kb][v] = -INFINITY;
+            sc[16 * kb + v] = (key >= lo && key <= hi) ? sc[16 * kb + v] : -INFINITY;
           }
       }
-      float tm = -INFINITY;
+      float tm = sc[0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tm = fmaxf(tm, sacc[kb][v]);
+      for (int e = 1; e < 32; ++e) tm = fmaxf(tm, sc[e]);
       tm = fmaxf(tm, __shfl_xor(tm, 32));
       const float mn = fmaxf(m, tm);
       const float mu = mn == -INFINITY ? 0.f : mn;
@@ -228,39 +270,29 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
       float ls = 0.f;
       bf16x8 pk[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pr = hw_exp2(fmaf(sacc[kb][8 * sub + e], c, -mc));
-            ls += pr;
-            pk[2 * kb + sub][e] = static_cast<__bf16>(pr);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const float pr = hw_exp2(fmaf(sc[8 * ks + e], c, -mc));
+          ls += pr;
+          pk[ks][e] = static_cast<__bf16>(pr);
+        }
       l = fmaf(l, alpha, ls);
       m = mn;
-      if (alpha != 1.0f) {
+      if (__any(alpha != 1.0f)) {     // wave-uniform: after the first tiles the max rarely moves
 #pragma unroll
         for (int j = 0; j < OB; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
       }
-      // O^T += V^T P^T; k-step (kb, sub) covers keys 32 kb + 16 sub + {4 hf .. +3, 8 + 4 hf .. +3}
+      // O^T += V^T P^T; k-step ks = 2 kb + sub covers keys 32 kb + 16 sub + {4 hf .. +3, 8 + 4 hf .. +3}
 #pragma unroll
-      for (int j = 0; j < OB; ++j) {
-        const __bf16* vrow = sv + (32 * j + q) * VST + 4 * hf;
+      for (int j = 0; j < OB; ++j)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 32 * kb + 16 * sub);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 32 * kb + 16 * sub + 8);
-            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[2 * kb + sub], o[j], 0, 0, 0);
-          }
-      }
+        for (int ks = 0; ks < 4; ++ks)
+          o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][ks], pk[ks], o[j], 0, 0, 0);
     }
-    if (more) store_tile(buf ^ 1, regs);
+    if (more) tile_store<HD>(regs, sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
     __syncthreads();
   }
 
@@ -286,7 +318,8 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnParams& p, int hd, hipStream_t stream) {
-  dim3 grid(ceil_div(p.max_seqlen, BM), p.H, p.S);
+  const int n_bh8 = ceil_div(p.S * p.H, 8) * 8;
+  dim3 grid(ceil_div(p.max_seqlen, BM) * n_bh8);
   if (hd == 64) {
     hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(NT), 0, stream, p);
   } else {
