@@ -146,7 +146,7 @@ typedef struct {
 } attamba_scan_args;
 
 /* Errors: NULL_ARG, BAD_SHAPE (T, n_chunks < 0; d not a positive multiple of 64),
- * BAD_DTYPE, UNSUPPORTED (N not 16 or 32), HIP. */
+ * BAD_DTYPE, UNSUPPORTED (N not 16 or 32, or T*d of 2^31 elements or more), HIP. */
 int attamba_kvssm_scan(const attamba_scan_args* args, attamba_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------

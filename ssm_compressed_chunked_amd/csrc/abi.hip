@@ -152,6 +152,8 @@ int attamba_kvssm_scan(const attamba_scan_args* a, attamba_stream_t stream) {
     return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan: T=%d n_chunks=%d", a->T, a->n_chunks);
   if (a->d <= 0 || a->d % 64 != 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan: d=%d not a positive multiple of 64", a->d);
   if (a->N != 16 && a->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "kvssm_scan: N=%d (16 or 32)", a->N);
+  if (static_cast<int64_t>(a->T) * a->d > INT32_MAX)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "kvssm_scan: T*d exceeds 2^31 elements");
   if (!a->chunk_cu || !a->x || !a->dt_k || !a->dt_v || !a->bm_k || !a->cm_k || !a->bm_v || !a->cm_v ||
       !a->A_k || !a->A_v || !a->D_k || !a->D_v || !a->bias_k || !a->bias_v || !a->y_k || !a->y_v)
     return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: a required pointer is null");

@@ -7,12 +7,15 @@
 // and the 2*N decay rates (A * log2 e) in VGPRs; a wave owns 64 consecutive channels and walks
 // a group of whole chunks token by token (chunks are independent because the state restarts
 // at every chunk start). All lanes of a wave sit on the same token, so the per-token rows
-// bm/cm (shared by all channels) are wave-uniform: they are fetched with scalar loads and
+// bm/cm (shared by all channels) are wave-uniform: the pointers are restrict-qualified kernel
+// arguments, so they are fetched with scalar loads, widened to float32 on the scalar unit and
 // enter the VALU instructions as SGPR operands. Per state and token the work is one multiply
-// for the exponent, one v_exp_f32, one multiply for the input term, one FMA for the state
-// and one FMA for the output; this instruction stream, not HBM, bounds the kernel. x and the
-// two step-size rows are read once per token for both SSMs (128-byte rows per wave at bf16),
-// the next token's row is prefetched while the current one is computed.
+// for the exponent, one v_exp_f32, one multiply for the input term, one FMA for the state and
+// one FMA for the output; this instruction stream, not HBM, bounds the kernel.
+// Chunks of the common length PU are processed fully unrolled: all x/dt loads of the chunk are
+// issued at its start, and no state value is carried across a loop back-edge (it restarts at
+// the next chunk anyway), so no register copies are needed. Other chunk lengths (random
+// chunking, a partial first or last chunk) take a token loop.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,28 +24,21 @@ namespace {
 
 constexpr int kChunksPerWave = 8;
 
-struct ScanParams {
+struct ScanShape {
   int T, d, n_chunks, S;
-  const int32_t* chunk_cu;
-  const void *x, *dt_k, *dt_v, *bm_k, *cm_k, *bm_v, *cm_v;
-  const float *A_k, *A_v, *D_k, *D_v, *bias_k, *bias_v;
-  void *y_k, *y_v, *kb, *vb;
-  const int32_t* seq_cu;
-  float *h_last_k, *h_last_v;
   int groups;          // chunk groups = ceil(n_chunks / kChunksPerWave)
   int ctiles;          // channel tiles = d / 64
-  int group_rows;      // ceil(groups / 8)
 };
 
 // Workgroup id -> (chunk group, channel tile). Workgroups are dispatched round-robin over
 // the 8 XCDs (id mod 8), each with its own L2; every channel tile of one chunk group is
 // placed on the same XCD so the group's bm/cm rows are fetched from HBM once per XCD.
-__device__ __forceinline__ bool map_block(const ScanParams& p, int& group, int& ctile) {
+__device__ __forceinline__ bool map_block(const ScanShape& sh, int& group, int& ctile) {
   const int id = blockIdx.x;
   const int xcd = id & 7, slot = id >> 3;
-  group = (slot / p.ctiles) * 8 + xcd;
-  ctile = slot % p.ctiles;
-  return group < p.groups;
+  group = (slot / sh.ctiles) * 8 + xcd;
+  ctile = slot % sh.ctiles;
+  return group < sh.groups;
 }
 
 template <typename T, int N>
@@ -51,117 +47,158 @@ struct SsmLane {
   float h[N];
   float D, bias;
 
-  __device__ __forceinline__ void load_params(const float* A, const float* Dp, const float* bp,
-                                              int c) {
+  __device__ __forceinline__ void load_params(const float* __restrict__ A,
+                                              const float* __restrict__ Dp,
+                                              const float* __restrict__ bp, int c) {
 #pragma unroll
     for (int n = 0; n < N; ++n) A2[n] = A[c * N + n] * kLog2e;
     D = Dp[c];
     bias = bp[c];
   }
 
-  // One token. FIRST: the state restarts (no decay term).
+  // One token. FIRST: the state restarts (no decay term). bm/cm point at the token's rows.
   template <bool FIRST>
   __device__ __forceinline__ float step(float x, float dt, const T* __restrict__ bm,
                                         const T* __restrict__ cm) {
+    float b[N], cc[N];
+    load_row(bm, b);
+    load_row(cm, cc);
     const float delta = softplus_f32(dt + bias);
     const float u = delta * x;
     float y = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      const float inj = u * to_f32(bm[n]);
+      const float inj = u * b[n];
       if (FIRST) {
         h[n] = inj;
       } else {
         h[n] = fmaf(hw_exp2(delta * A2[n]), h[n], inj);
       }
-      y = fmaf(h[n], to_f32(cm[n]), y);
+      y = fmaf(h[n], cc[n], y);
     }
     return fmaf(D, x, y);
   }
+
+  // A wave-uniform row of N values, read as 32-bit words so that the compiler issues scalar
+  // loads (bf16 pairs are split with shifts on the scalar unit).
+  static __device__ __forceinline__ void load_row(const T* __restrict__ row, float (&v)[N]) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(row);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int n = 0; n < N / 2; ++n) {
+        const uint32_t p = w[n];
+        v[2 * n] = __uint_as_float(p << 16);
+        v[2 * n + 1] = __uint_as_float(p & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) v[n] = __uint_as_float(w[n]);
+    }
+  }
 };
 
-template <typename T, int N>
-__global__ __launch_bounds__(kWave) void kvssm_scan_kernel(ScanParams p) {
+template <typename T, int N, int PU>
+__global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
+    ScanShape sh, const int32_t* __restrict__ chunk_cu, const T* __restrict__ x,
+    const T* __restrict__ dtk, const T* __restrict__ dtv, const T* __restrict__ bmk,
+    const T* __restrict__ cmk, const T* __restrict__ bmv, const T* __restrict__ cmv,
+    const float* __restrict__ A_k, const float* __restrict__ A_v, const float* __restrict__ D_k,
+    const float* __restrict__ D_v, const float* __restrict__ bias_k,
+    const float* __restrict__ bias_v, T* __restrict__ yk, T* __restrict__ yv,
+    T* __restrict__ kb, T* __restrict__ vb, const int32_t* __restrict__ seq_cu,
+    float* __restrict__ h_last_k, float* __restrict__ h_last_v) {
   int group, ctile;
-  if (!map_block(p, group, ctile)) return;
+  if (!map_block(sh, group, ctile)) return;
   const int lane = threadIdx.x;
   const int c = ctile * kWave + lane;
-  const int d = p.d;
+  const int d = sh.d;
   const int q0 = group * kChunksPerWave;
-  const int q1 = min(q0 + kChunksPerWave, p.n_chunks);
-
-  const T* __restrict__ x = static_cast<const T*>(p.x);
-  const T* __restrict__ dtk = static_cast<const T*>(p.dt_k);
-  const T* __restrict__ dtv = static_cast<const T*>(p.dt_v);
-  const T* __restrict__ bmk = static_cast<const T*>(p.bm_k);
-  const T* __restrict__ cmk = static_cast<const T*>(p.cm_k);
-  const T* __restrict__ bmv = static_cast<const T*>(p.bm_v);
-  const T* __restrict__ cmv = static_cast<const T*>(p.cm_v);
-  T* __restrict__ yk = static_cast<T*>(p.y_k);
-  T* __restrict__ yv = static_cast<T*>(p.y_v);
-  T* __restrict__ kb = static_cast<T*>(p.kb);
-  T* __restrict__ vb = static_cast<T*>(p.vb);
+  const int q1 = min(q0 + kChunksPerWave, sh.n_chunks);
 
   SsmLane<T, N> sk, sv;
-  sk.load_params(p.A_k, p.D_k, p.bias_k, c);
-  sv.load_params(p.A_v, p.D_v, p.bias_v, c);
+  sk.load_params(A_k, D_k, bias_k, c);
+  sv.load_params(A_v, D_v, bias_v, c);
 
-  const int tb = p.chunk_cu[q0];
-  const int te = p.chunk_cu[q1];
-  int q = q0;
-  int cs = tb;                      // start of chunk q
-  int ce = p.chunk_cu[q0 + 1];      // end (exclusive) of chunk q
-
-  float nx = 0.f, ndk = 0.f, ndv = 0.f;
-  if (tb < te) {
-    const size_t o = static_cast<size_t>(tb) * d + c;
-    nx = to_f32(x[o]); ndk = to_f32(dtk[o]); ndv = to_f32(dtv[o]);
-  }
-  for (int t = tb; t < te; ++t) {
-    const float xv = nx, dk = ndk, dv = ndv;
-    if (t + 1 < te) {
-      const size_t o = static_cast<size_t>(t + 1) * d + c;
-      nx = to_f32(x[o]); ndk = to_f32(dtk[o]); ndv = to_f32(dtv[o]);
+  // end of chunk q: boundary state and, for the last chunk of a sequence, the hand-off state
+  auto chunk_end = [&](int q, int cs, int ce, float ok, float ov) {
+    if (kb) {
+      kb[q * d + c] = from_f32<T>(ok);
+      vb[q * d + c] = from_f32<T>(ov);
     }
-    const size_t rN = static_cast<size_t>(t) * N;
-    float ok, ov;
-    if (t == cs) {
-      ok = sk.template step<true>(xv, dk, bmk + rN, cmk + rN);
-      ov = sv.template step<true>(xv, dv, bmv + rN, cmv + rN);
-    } else {
-      ok = sk.template step<false>(xv, dk, bmk + rN, cmk + rN);
-      ov = sv.template step<false>(xv, dv, bmv + rN, cmv + rN);
-    }
-    const size_t o = static_cast<size_t>(t) * d + c;
-    yk[o] = from_f32<T>(ok);
-    yv[o] = from_f32<T>(ov);
-    if (t == ce - 1) {              // last token of chunk q: boundary state and hand-off
-      if (kb) kb[static_cast<size_t>(q) * d + c] = from_f32<T>(ok);
-      if (vb) vb[static_cast<size_t>(q) * d + c] = from_f32<T>(ov);
-      if (p.h_last_k) {
-        int lo = 0, hi = p.S;       // sequence s with seq_cu[s] <= cs < seq_cu[s + 1]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (p.seq_cu[mid] <= cs) lo = mid; else hi = mid;
-        }
-        if (p.seq_cu[lo + 1] == ce) {
-          float* hk = p.h_last_k + (static_cast<size_t>(lo) * d + c) * N;
-          float* hv = p.h_last_v + (static_cast<size_t>(lo) * d + c) * N;
-#pragma unroll
-          for (int n = 0; n < N; ++n) { hk[n] = sk.h[n]; hv[n] = sv.h[n]; }
-        }
+    if (h_last_k) {
+      int lo = 0, hi = sh.S;        // sequence s with seq_cu[s] <= cs < seq_cu[s + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (seq_cu[mid] <= cs) lo = mid; else hi = mid;
       }
-      ++q;
-      cs = ce;
-      if (q < q1) ce = p.chunk_cu[q + 1];
+      if (seq_cu[lo + 1] == ce) {
+        float* hk = h_last_k + (static_cast<size_t>(lo) * d + c) * N;
+        float* hv = h_last_v + (static_cast<size_t>(lo) * d + c) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) { hk[n] = sk.h[n]; hv[n] = sv.h[n]; }
+      }
     }
+  };
+
+  int cs = chunk_cu[q0];
+  for (int q = q0; q < q1; ++q) {
+    const int ce = chunk_cu[q + 1];
+    float ok = 0.f, ov = 0.f;
+    if (ce - cs == PU) {
+      float xs[PU], dks[PU], dvs[PU];
+#pragma unroll
+      for (int j = 0; j < PU; ++j) {
+        const int o = (cs + j) * d + c;
+        xs[j] = to_f32(x[o]); dks[j] = to_f32(dtk[o]); dvs[j] = to_f32(dtv[o]);
+      }
+#pragma unroll
+      for (int j = 0; j < PU; ++j) {
+        const int t = cs + j;
+        if (j == 0) {
+          ok = sk.template step<true>(xs[j], dks[j], bmk + t * N, cmk + t * N);
+          ov = sv.template step<true>(xs[j], dvs[j], bmv + t * N, cmv + t * N);
+        } else {
+          ok = sk.template step<false>(xs[j], dks[j], bmk + t * N, cmk + t * N);
+          ov = sv.template step<false>(xs[j], dvs[j], bmv + t * N, cmv + t * N);
+        }
+        yk[t * d + c] = from_f32<T>(ok);
+        yv[t * d + c] = from_f32<T>(ov);
+      }
+    } else {
+      float nx = to_f32(x[cs * d + c]), ndk = to_f32(dtk[cs * d + c]), ndv = to_f32(dtv[cs * d + c]);
+      for (int t = cs; t < ce; ++t) {
+        const float xv = nx, dk = ndk, dv = ndv;
+        if (t + 1 < ce) {
+          const int o = (t + 1) * d + c;
+          nx = to_f32(x[o]); ndk = to_f32(dtk[o]); ndv = to_f32(dtv[o]);
+        }
+        if (t == cs) {
+          ok = sk.template step<true>(xv, dk, bmk + t * N, cmk + t * N);
+          ov = sv.template step<true>(xv, dv, bmv + t * N, cmv + t * N);
+        } else {
+          ok = sk.template step<false>(xv, dk, bmk + t * N, cmk + t * N);
+          ov = sv.template step<false>(xv, dv, bmv + t * N, cmv + t * N);
+        }
+        yk[t * d + c] = from_f32<T>(ok);
+        yv[t * d + c] = from_f32<T>(ov);
+      }
+    }
+    chunk_end(q, cs, ce, ok, ov);
+    cs = ce;
   }
 }
 
 template <typename T, int N>
-hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
-  const int blocks = p.group_rows * 8 * p.ctiles;
-  hipLaunchKernelGGL((kvssm_scan_kernel<T, N>), dim3(blocks), dim3(kWave), 0, stream, p);
+hipError_t launch_typed(const attamba_scan_args& a, const ScanShape& sh, hipStream_t stream) {
+  const int blocks = ceil_div(sh.groups, 8) * 8 * sh.ctiles;
+  hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8>), dim3(blocks), dim3(kWave), 0, stream, sh,
+                     a.chunk_cu, static_cast<const T*>(a.x), static_cast<const T*>(a.dt_k),
+                     static_cast<const T*>(a.dt_v), static_cast<const T*>(a.bm_k),
+                     static_cast<const T*>(a.cm_k), static_cast<const T*>(a.bm_v),
+                     static_cast<const T*>(a.cm_v), a.A_k, a.A_v, a.D_k, a.D_v, a.bias_k,
+                     a.bias_v, static_cast<T*>(a.y_k), static_cast<T*>(a.y_v),
+                     static_cast<T*>(a.kb), static_cast<T*>(a.vb), a.seq_cu, a.h_last_k,
+                     a.h_last_v);
   return hipGetLastError();
 }
 
@@ -169,23 +206,14 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
 
 hipError_t launch_kvssm_scan(const attamba_scan_args& a, hipStream_t stream) {
   if (a.n_chunks == 0 || a.T == 0) return hipSuccess;
-  ScanParams p;
-  p.T = a.T; p.d = a.d; p.n_chunks = a.n_chunks; p.S = a.S;
-  p.chunk_cu = a.chunk_cu;
-  p.x = a.x; p.dt_k = a.dt_k; p.dt_v = a.dt_v;
-  p.bm_k = a.bm_k; p.cm_k = a.cm_k; p.bm_v = a.bm_v; p.cm_v = a.cm_v;
-  p.A_k = a.A_k; p.A_v = a.A_v; p.D_k = a.D_k; p.D_v = a.D_v;
-  p.bias_k = a.bias_k; p.bias_v = a.bias_v;
-  p.y_k = a.y_k; p.y_v = a.y_v; p.kb = a.kb; p.vb = a.vb;
-  p.seq_cu = a.seq_cu;
-  p.h_last_k = a.h_last_k; p.h_last_v = a.h_last_v;
-  p.groups = ceil_div(a.n_chunks, kChunksPerWave);
-  p.ctiles = a.d / kWave;
-  p.group_rows = ceil_div(p.groups, 8);
+  ScanShape sh;
+  sh.T = a.T; sh.d = a.d; sh.n_chunks = a.n_chunks; sh.S = a.S;
+  sh.groups = ceil_div(a.n_chunks, kChunksPerWave);
+  sh.ctiles = a.d / kWave;
   if (a.dtype == ATTAMBA_BF16) {
-    return a.N == 16 ? launch_typed<__bf16, 16>(p, stream) : launch_typed<__bf16, 32>(p, stream);
+    return a.N == 16 ? launch_typed<__bf16, 16>(a, sh, stream) : launch_typed<__bf16, 32>(a, sh, stream);
   }
-  return a.N == 16 ? launch_typed<float, 16>(p, stream) : launch_typed<float, 32>(p, stream);
+  return a.N == 16 ? launch_typed<float, 16>(a, sh, stream) : launch_typed<float, 32>(a, sh, stream);
 }
 
 }  // namespace attamba
