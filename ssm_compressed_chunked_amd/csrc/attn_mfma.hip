@@ -5,23 +5,26 @@
 // Workgroup = 4 waves = 128 query rows of one (sequence, head); wave = 32 rows. Keys come in
 // tiles of 64, first the compact boundary states kb/vb (chunks that end before the window of
 // the workgroup's last row), then the per-token keys of the band [w(first row), last row].
-// Each tile is staged in LDS (double-buffered: the next tile's global loads are in flight
-// while the current one is computed):
-//   K rows as they are in memory ([key][hd], rows padded to 16 B past hd so that the 32 key
-//   rows a wave reads with ds_read_b128 fall on distinct banks);
-//   V transposed to [hd][key] (rows padded by 8 B) so that the PV operand is two 8-byte reads.
+//
+// Tiles go from HBM straight into LDS with global_load_lds_dwordx4 (no VGPR staging): the
+// next tile's copy is in flight while the current tile is computed (double buffer, one
+// barrier per tile). K and V tiles are stored row-major ([key][hd]) with the 16-byte segments
+// of each row permuted by an XOR swizzle of the row index, so that both read patterns below
+// hit distinct LDS banks without padding (padding is impossible: a wave's LDS-direct copy
+// fills 1 KB contiguously).
 // Per tile and wave:
-//   S^T (keys x queries) = K Q^T        v_mfma_f32_32x32x16_bf16, Q held in registers
+//   S^T (keys x queries) = K Q^T        v_mfma_f32_32x32x16_bf16; Q in registers, the K
+//                                        operand is one ds_read_b128 per (key block, k-step);
 //   online softmax in float32 per query (one lane per query and key half; the two halves
 //   meet with one cross-lane max per tile), masking only in tiles that straddle a row's
-//   visible range and skipping tiles no row of the wave can see;
-//   O^T (hd x queries) += V^T P^T       v_mfma_f32_32x32x16_bf16.
+//   visible range, skipping tiles no row of the wave can see;
+//   O^T (hd x queries) += V^T P^T       v_mfma_f32_32x32x16_bf16; the V^T operand comes from
+//                                        the row-major V tile through two ds_read_b64_tr_b16
+//                                        (the gfx950 transposing LDS read) per k-step.
 // S^T puts one query per lane, so the softmax statistics, the rescale of O^T and the final
 // division are per-lane operations; the P operand of the second product is the first
-// product's accumulator converted to bf16 in place (the keys are taken in the accumulator's
-// row order, and V^T is read in the same order).
-#include <climits>
-
+// product's accumulator converted to bf16 in place (keys taken in the accumulator's row order;
+// the V^T operand is read in the same order).
 #include "common.h"
 #include "kernels.h"
 
@@ -30,7 +33,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
@@ -54,74 +60,51 @@ __device__ __forceinline__ Geo geo(const AttnParams& p, int i, int s0, int s1, i
   return g;
 }
 
+// Row r of a tile keeps its 16-byte segment s at position s ^ swz(r). The K read (16 lanes,
+// one segment, 16 consecutive rows) and the transposing V read (16 lanes, two adjacent
+// segments, 4 consecutive rows starting at a multiple of 4) then touch distinct bank groups.
 template <int HD>
-struct Smem {
-  static constexpr int KST = HD + 8;   // K row stride (elements)
-  static constexpr int VST = BN + 4;   // V^T row stride (elements)
-  __bf16 k[2][BN * KST];
-  __bf16 v[2][HD * VST];
-};
-
-template <int HD>
-struct TileRegs {
-  static constexpr int KU = BN * HD / 8 / NT;        // 16-byte K pieces per thread
-  static constexpr int VU = (HD / 8) * (BN / 2) / NT; // (hd group, key pair) units per thread
-  uint4 k[KU];
-  uint4 v0[VU], v1[VU];
-};
-
-// Global -> registers for one tile of keys base .. base + BN - 1. Keys past `top` (the last
-// valid key) re-read row `top` instead of branching around the load: every row that could
-// see such a key masks it. Offsets are 32-bit (element counts below 2^31, checked at the ABI).
-template <int HD>
-__device__ __forceinline__ void tile_load(TileRegs<HD>& r, const __bf16* __restrict__ kp,
-                                          const __bf16* __restrict__ vp, int base, int top,
-                                          int hs, int tid) {
-#pragma unroll
-  for (int u = 0; u < TileRegs<HD>::KU; ++u) {
-    const int piece = tid + u * NT;
-    const int key = piece / (HD / 8), seg = piece % (HD / 8);
-    const int kk = min(base + key, top);
-    r.k[u] = *reinterpret_cast<const uint4*>(kp + (kk * hs + seg * 8));
-  }
-#pragma unroll
-  for (int u = 0; u < TileRegs<HD>::VU; ++u) {
-    const int unit = tid + u * NT;
-    const int gq = unit % (HD / 8), kp2 = unit / (HD / 8);
-    const int k0 = min(base + 2 * kp2, top), k1 = min(base + 2 * kp2 + 1, top);
-    r.v0[u] = *reinterpret_cast<const uint4*>(vp + (k0 * hs + gq * 8));
-    r.v1[u] = *reinterpret_cast<const uint4*>(vp + (k1 * hs + gq * 8));
-  }
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (HD == 64) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  else return 2 * (r & 7) + ((r >> 3) & 1);
 }
 
-// Registers -> LDS: K rows as they are; V transposed to [hd][key], two keys per 32-bit word.
+// element offset of (row r, element e) in a tile
 template <int HD>
-__device__ __forceinline__ void tile_store(const TileRegs<HD>& r, __bf16* sk, __bf16* sv, int tid) {
-  constexpr int KST = Smem<HD>::KST, VST = Smem<HD>::VST;
+__device__ __forceinline__ int tile_off(int r, int e) {
+  return r * HD + 8 * ((e >> 3) ^ swz<HD>(r)) + (e & 7);
+}
+
+template <int HD>
+struct Smem {
+  __bf16 k[2][BN * HD];
+  __bf16 v[2][BN * HD];
+};
+
+// Issue the LDS-direct copies of one tile (keys base .. base + BN - 1; keys past `top`, the last
+// valid key, re-read row `top`: every row that could see such a key masks it). Each wave copies
+// NI chunks of 1 KB; lane l of chunk ch fills 16-byte slot ch * 64 + l of the tile.
+template <int HD>
+__device__ __forceinline__ void tile_issue(__bf16* sk, __bf16* sv, const __bf16* kp,
+                                           const __bf16* vp, int base, int top, int hs, int wid,
+                                           int lane) {
+  constexpr int SPR = HD / 8;                    // 16-byte segments per row
+  constexpr int NI = BN * SPR / kWave / 4;       // 1 KB chunks per wave
 #pragma unroll
-  for (int u = 0; u < TileRegs<HD>::KU; ++u) {
-    const int piece = tid + u * NT;
-    const int key = piece / (HD / 8), seg = piece % (HD / 8);
-    *reinterpret_cast<uint4*>(sk + key * KST + seg * 8) = r.k[u];
-  }
-#pragma unroll
-  for (int u = 0; u < TileRegs<HD>::VU; ++u) {
-    const int unit = tid + u * NT;
-    const int gq = unit % (HD / 8), kp2 = unit / (HD / 8);
-    const uint32_t a[4] = {r.v0[u].x, r.v0[u].y, r.v0[u].z, r.v0[u].w};
-    const uint32_t b[4] = {r.v1[u].x, r.v1[u].y, r.v1[u].z, r.v1[u].w};
-    uint32_t* dst = reinterpret_cast<uint32_t*>(sv + (gq * 8) * VST + 2 * kp2);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      dst[(2 * e2) * (VST / 2)] = (a[e2] & 0xffffu) | (b[e2] << 16);
-      dst[(2 * e2 + 1) * (VST / 2)] = (a[e2] >> 16) | (b[e2] & 0xffff0000u);
-    }
+  for (int i = 0; i < NI; ++i) {
+    const int ch = wid * NI + i;
+    const int slot = ch * kWave + lane;
+    const int r = slot / SPR, pos = slot % SPR;
+    const int seg = pos ^ swz<HD>(r);
+    const int key = min(base + r, top);
+    const int go = key * hs + seg * 8;
+    __builtin_amdgcn_global_load_lds(kp + go, LDS_PTR(void, sk + ch * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + go, LDS_PTR(void, sv + ch * 512), 16, 0, 0);
   }
 }
 
 template <int HD>
 __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
-  constexpr int KST = Smem<HD>::KST, VST = Smem<HD>::VST;
   constexpr int QS = HD / 16;     // k-steps of S^T (16 hd each)
   constexpr int OB = HD / 32;     // 32-row hd blocks of O^T
   __shared__ Smem<HD> sm;
@@ -143,7 +126,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const int q = lane & 31, hf = lane >> 5;
   const int last = min(r0 + BM, s1) - 1;
   const int c0 = p.token_chunk[s0];
-  const size_t hs = static_cast<size_t>(p.H) * HD;   // row stride of [., H, HD]
+  const int hs = p.H * HD;   // row stride of [., H, HD]; T * H * HD < 2^31 (checked at the ABI)
 
   // this lane's row, and the wave's row range (rows past the sequence mimic its last row)
   const int i = r0 + wid * 32 + q;
@@ -160,6 +143,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const int band0 = gf.w;
   const int nbd = last >= band0 ? ceil_div(last - band0 + 1, BN) : 0;
   const int ntiles = nbt + nbd;
+  const int topb = c0 + gl.E - 1;   // last boundary key of the workgroup
 
   // Q^T operand: lane (q, hf) holds hd 16 st + 8 hf .. +7 of its row
   bf16x8 qf[QS];
@@ -173,7 +157,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   for (int j = 0; j < OB; ++j)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[j][v] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float mc = -INFINITY, l = 0.f;   // exponent reference (log2 units) and running sum
   const float c = p.scale * kLog2e;
 
   const __bf16* kbp = static_cast<const __bf16*>(p.kb) + h * HD;
@@ -181,25 +165,44 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const __bf16* ktp = static_cast<const __bf16*>(p.k) + h * HD;
   const __bf16* vtp = static_cast<const __bf16*>(p.v) + h * HD;
 
-  const int hs32 = p.H * HD;
-  const int topb = c0 + gl.E - 1;   // last boundary key of the workgroup
-  // tile t: boundary tiles first, then band tiles
-  auto src_k = [&](int t) { return t < nbt ? kbp : ktp; };
-  auto src_v = [&](int t) { return t < nbt ? vbp : vtp; };
-  auto base_of = [&](int t) { return t < nbt ? c0 + t * BN : band0 + (t - nbt) * BN; };
-  auto top_of = [&](int t) { return t < nbt ? topb : last; };
-  TileRegs<HD> regs;
-  if (ntiles > 0) {
-    tile_load<HD>(regs, src_k(0), src_v(0), base_of(0), top_of(0), hs32, tid);
-    tile_store<HD>(regs, sm.k[0], sm.v[0], tid);
+  // per-lane LDS element offsets that do not depend on the tile
+  int koff[2][QS];                 // S^T operand: row 32 kb + q, segment 2 st + hf
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int st = 0; st < QS; ++st) koff[kb][st] = tile_off<HD>(32 * kb + q, 16 * st + 8 * hf);
+  int voff[OB][4][2];              // V^T operand: rows K0 + (lane%16)/4, K0 = 16 ks + 4 hf (+8)
+  {
+    const int sl = lane & 15, g16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int j = 0; j < OB; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int row = 16 * ks + 8 * half + 4 * hf + (sl >> 2);
+          const int col = 32 * j + 16 * g16 + 4 * (sl & 3);
+          voff[j][ks][half] = tile_off<HD>(row, col);
+        }
   }
+
+  if (ntiles > 0) {
+    const bool b0 = nbt > 0;
+    tile_issue<HD>(sm.k[0], sm.v[0], b0 ? kbp : ktp, b0 ? vbp : vtp, b0 ? c0 : band0,
+                   b0 ? topb : last, hs, wid, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
-    const int tn = more ? t + 1 : t;
-    tile_load<HD>(regs, src_k(tn), src_v(tn), base_of(tn), top_of(tn), hs32, tid);
+    if (t + 1 < ntiles) {
+      const int tn = t + 1;
+      const bool bn = tn < nbt;
+      tile_issue<HD>(sm.k[buf ^ 1], sm.v[buf ^ 1], bn ? kbp : ktp, bn ? vbp : vtp,
+                     bn ? c0 + tn * BN : band0 + (tn - nbt) * BN, bn ? topb : last, hs, wid,
+                     lane);
+    }
 
     // which rows of this wave see which keys of the tile
     const bool bnd = t < nbt;
@@ -215,85 +218,95 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
     if (!skip) {
       const __bf16* sk = sm.k[buf];
       const __bf16* sv = sm.v[buf];
-      bf16x8 ka[2][QS];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < QS; ++st)
-          ka[kb][st] = *reinterpret_cast<const bf16x8*>(sk + (32 * kb + q) * KST + 16 * st + 8 * hf);
+      // The mask enters as the initial accumulator of S^T: 0 for a visible key, -inf for a
+      // hidden one (accumulator row v of block kb is key base + 4 hf + C(kb, v),
+      // C = 32 kb + 8 (v / 4) + v % 4).
       f32x16 sacc[2];
+      auto qk = [&](f32x16 (&acc)[2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+          for (int st = 0; st < QS; ++st)
+            acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8*>(sk + koff[kb][st]), qf[st], acc[kb], 0, 0, 0);
+      };
+      if (full) {
 #pragma unroll
-        for (int st = 0; st < QS; ++st)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][st], qf[st], sacc[kb], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+        qk(sacc);
+      } else {
+        const int kbase = base + 4 * hf;
+        // visible iff lo <= C <= hi (boundary tiles: below c0 + E; band tiles: w .. i)
+        const int lo = bnd ? -(1 << 30) : g.w - kbase;
+        const int hi = bnd ? c0 + g.E - 1 - kbase : ic - kbase;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
+            sacc[kb][v] = (C >= lo && C <= hi) ? 0.f : -INFINITY;
+          }
+        qk(sacc);
       }
       // V^T fragments of this tile (read while the products above drain)
       bf16x8 va[OB][4];
 #pragma unroll
-      for (int j = 0; j < OB; ++j) {
-        const __bf16* vrow = sv + (32 * j + q) * VST + 4 * hf;
+      for (int j = 0; j < OB; ++j)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * ks);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16 * ks + 8);
-          va[j][ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][0]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][1]));
+          const i16x4 both[2] = {lo, hi};
+          va[j][ks] = *reinterpret_cast<const bf16x8*>(both);
         }
-      }
-      // accumulator row v of block kb is key 32 kb + 8 (v / 4) + 4 hf + v % 4
       float sc[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sc[16 * kb + v] = sacc[kb][v];
-      if (!full) {
-        const int lo = bnd ? INT_MIN : g.w;
-        const int hi = bnd ? c0 + g.E - 1 : ic;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = base + 32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3);
-            sc[16 * kb + v] = (key >= lo && key <= hi) ? sc[16 * kb + v] : -INFINITY;
-          }
-      }
       float tm = sc[0];
 #pragma unroll
       for (int e = 1; e < 32; ++e) tm = fmaxf(tm, sc[e]);
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mn = fmaxf(m, tm);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = hw_exp2((m - mu) * c);
-      const float mc = mu * c;
-      float ls = 0.f;
-      bf16x8 pk[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pr = hw_exp2(fmaf(sc[8 * ks + e], c, -mc));
-          ls += pr;
-          pk[ks][e] = static_cast<__bf16>(pr);
-        }
-      l = fmaf(l, alpha, ls);
-      m = mn;
-      if (__any(alpha != 1.0f)) {     // wave-uniform: after the first tiles the max rarely moves
+      tm = fmaxf(tm, __shfl_xor(tm, 32)) * c;
+      // The exponent reference mc (log2 units) moves only when a row's maximum exceeds it by
+      // more than 8, so p <= 2^8 and the rescale of O^T and l is rare; exact either way, since
+      // l and O^T share the reference.
+      if (__any(tm > mc + 8.0f)) {
+        const float mn = fmaxf(mc, tm);
+        // 0 when mc = -inf (nothing accumulated yet), also for rows that still see no key
+        const float alpha = hw_exp2(mc - (mn == -INFINITY ? 0.f : mn));
 #pragma unroll
         for (int j = 0; j < OB; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
+        l *= alpha;
+        mc = mn;
       }
-      // O^T += V^T P^T; k-step ks = 2 kb + sub covers keys 32 kb + 16 sub + {4 hf .. +3, 8 + 4 hf .. +3}
+      const float mu = mc == -INFINITY ? 0.f : mc;
+      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      bf16x8 pk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = hw_exp2(fmaf(sc[8 * ks + e], c, -mu));
+          const float p1 = hw_exp2(fmaf(sc[8 * ks + e + 1], c, -mu));
+          const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+          l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);   // sum of the rounded p
+          pk[ks][e] = pp[0];
+          pk[ks][e + 1] = pp[1];
+        }
+      // O^T += V^T P^T; k-step ks = 2 kb + sub covers keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}
 #pragma unroll
       for (int j = 0; j < OB; ++j)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][ks], pk[ks], o[j], 0, 0, 0);
     }
-    if (more) tile_store<HD>(regs, sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile t + 1 have landed
+    __syncthreads();                  // ... and every wave is done with tile t
   }
 
   // epilogue: combine the two key halves of every query, normalise, write O and LSE
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
         *reinterpret_cast<bf16x4*>(orow + 32 * j + 8 * gq) = vv;
       }
     if (p.lse && hf == 0)
-      p.lse[static_cast<size_t>(h) * p.T + i] = lt > 0.f ? (m * c + hw_log2(lt)) * kLn2 : -INFINITY;
+      p.lse[static_cast<size_t>(h) * p.T + i] = lt > 0.f ? (mc + hw_log2(lt)) * kLn2 : -INFINITY;
   }
 }
 
