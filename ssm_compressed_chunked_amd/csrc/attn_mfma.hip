@@ -28,6 +28,7 @@
 #include "common.h"
 #include "kernels.h"
 
+
 namespace attamba {
 namespace {
 
@@ -38,7 +39,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr int NT = 256;   // threads per workgroup
 
@@ -69,17 +69,41 @@ __device__ __forceinline__ int swz(int r) {
   else return 2 * (r & 7) + ((r >> 3) & 1);
 }
 
+// max of x over lanes q and q + 32 (the two key halves of one query): v_permlane32_swap
+// exchanges the upper half of one register with the lower half of another.
+__device__ __forceinline__ float half_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // element offset of (row r, element e) in a tile
 template <int HD>
 __device__ __forceinline__ int tile_off(int r, int e) {
   return r * HD + 8 * ((e >> 3) ^ swz<HD>(r)) + (e & 7);
 }
 
+#ifndef ATTN_NBUF
+#define ATTN_NBUF 2
+#endif
+constexpr int NBUF = ATTN_NBUF;   // tiles in LDS: the current one and the copies in flight
+
 template <int HD>
 struct Smem {
-  __bf16 k[2][BN * HD];
-  __bf16 v[2][BN * HD];
+  __bf16 k[NBUF][BN * HD];
+  __bf16 v[NBUF][BN * HD];
 };
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
+// outstanding (LDS/scalar and export counters left unconstrained).
+__host__ __device__ constexpr int vmcnt_at_most(int n) {
+  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
+}
 
 // Issue the LDS-direct copies of one tile (keys base .. base + BN - 1; keys past `top`, the last
 // valid key, re-read row `top`: every row that could see such a key masks it). Each wave copies
@@ -107,6 +131,7 @@ template <int HD>
 __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   constexpr int QS = HD / 16;     // k-steps of S^T (16 hd each)
   constexpr int OB = HD / 32;     // 32-row hd blocks of O^T
+  constexpr int BM = 128;         // query rows per workgroup (4 waves x 32)
   __shared__ Smem<HD> sm;
 
   // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. All query tiles
@@ -130,8 +155,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
 
   // this lane's row, and the wave's row range (rows past the sequence mimic its last row)
   const int i = r0 + wid * 32 + q;
-  const bool valid = i < s1;
-  const int ic = valid ? i : last;
+  const int ic = min(i, last);
   const Geo g = geo(p, ic, s0, s1, c0);
   const int wr0 = min(r0 + wid * 32, last), wr1 = min(r0 + wid * 32 + 31, last);
   const int Ew0 = __shfl(g.E, 0), Ew1 = __shfl(g.E, 31);
@@ -157,7 +181,9 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   for (int j = 0; j < OB; ++j)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[j][v] = 0.f;
-  float mc = -INFINITY, l = 0.f;   // exponent reference (log2 units) and running sum
+  // Softmax state of the row: exponent reference mc (log2 units; -inf until the row has seen
+  // a key) and the running sum l of p = 2^(s c - mc) over this lane's keys.
+  float mc = -INFINITY, l = 0.f;
   const float c = p.scale * kLog2e;
 
   const __bf16* kbp = static_cast<const __bf16*>(p.kb) + h * HD;
@@ -186,23 +212,26 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
         }
   }
 
-  if (ntiles > 0) {
-    const bool b0 = nbt > 0;
-    tile_issue<HD>(sm.k[0], sm.v[0], b0 ? kbp : ktp, b0 ? vbp : vtp, b0 ? c0 : band0,
-                   b0 ? topb : last, hs, wid, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
+  auto issue = [&](int t) {
+    const bool bt = t < nbt;
+    const int buf = t % NBUF;
+    tile_issue<HD>(sm.k[buf], sm.v[buf], bt ? kbp : ktp, bt ? vbp : vtp,
+                   bt ? c0 + t * BN : band0 + (t - nbt) * BN, bt ? topb : last, hs, wid, lane);
+  };
+  constexpr int kLoadsPerTile = 2 * (BN * (HD / 8) / kWave / 4);   // per wave
+  constexpr int kAhead = NBUF - 1;                                 // tiles in flight
+#pragma unroll
+  for (int a = 0; a < kAhead; ++a)
+    if (a < ntiles) issue(a);
+  if (ntiles > kAhead) __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kAhead - 1) * kLoadsPerTile));
+  else __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  const f32x16 zero16 = {};
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      const int tn = t + 1;
-      const bool bn = tn < nbt;
-      tile_issue<HD>(sm.k[buf ^ 1], sm.v[buf ^ 1], bn ? kbp : ktp, bn ? vbp : vtp,
-                     bn ? c0 + tn * BN : band0 + (tn - nbt) * BN, bn ? topb : last, hs, wid,
-                     lane);
-    }
+    const int buf = t % NBUF;
+    if (t + kAhead < ntiles) issue(t + kAhead);
 
     // which rows of this wave see which keys of the tile
     const bool bnd = t < nbt;
@@ -218,101 +247,108 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
     if (!skip) {
       const __bf16* sk = sm.k[buf];
       const __bf16* sv = sm.v[buf];
-      // The mask enters as the initial accumulator of S^T: 0 for a visible key, -inf for a
-      // hidden one (accumulator row v of block kb is key base + 4 hf + C(kb, v),
-      // C = 32 kb + 8 (v / 4) + v % 4).
+      // S^T = K Q^T. The mask enters as the initial accumulator: 0 for a visible key, -inf for
+      // a hidden one (accumulator row v of block kb is key base + 4 hf + C(kb, v),
+      // C = 32 kb + 8 (v / 4) + v % 4); full tiles start from the zero accumulator.
       f32x16 sacc[2];
-      auto qk = [&](f32x16 (&acc)[2]) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int st = 0; st < QS; ++st)
-            acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *reinterpret_cast<const bf16x8*>(sk + koff[kb][st]), qf[st], acc[kb], 0, 0, 0);
-      };
       if (full) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          bf16x8 ka[QS];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-        qk(sacc);
+          for (int st = 0; st < QS; ++st) ka[st] = *reinterpret_cast<const bf16x8*>(sk + koff[kb][st]);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], zero16, 0, 0, 0);
+#pragma unroll
+          for (int st = 1; st < QS; ++st)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], sacc[kb], 0, 0, 0);
+        }
       } else {
         const int kbase = base + 4 * hf;
         // visible iff lo <= C <= hi (boundary tiles: below c0 + E; band tiles: w .. i)
         const int lo = bnd ? -(1 << 30) : g.w - kbase;
         const int hi = bnd ? c0 + g.E - 1 - kbase : ic - kbase;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          bf16x8 ka[QS];
+#pragma unroll
+          for (int st = 0; st < QS; ++st) ka[st] = *reinterpret_cast<const bf16x8*>(sk + koff[kb][st]);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
             sacc[kb][v] = (C >= lo && C <= hi) ? 0.f : -INFINITY;
           }
-        qk(sacc);
-      }
-      // V^T fragments of this tile (read while the products above drain)
-      bf16x8 va[OB][4];
 #pragma unroll
-      for (int j = 0; j < OB; ++j)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][0]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][1]));
-          const i16x4 both[2] = {lo, hi};
-          va[j][ks] = *reinterpret_cast<const bf16x8*>(both);
+          for (int st = 0; st < QS; ++st)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], sacc[kb], 0, 0, 0);
         }
-      float sc[32];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sc[16 * kb + v] = sacc[kb][v];
-      float tm = sc[0];
-#pragma unroll
-      for (int e = 1; e < 32; ++e) tm = fmaxf(tm, sc[e]);
-      tm = fmaxf(tm, __shfl_xor(tm, 32)) * c;
-      // The exponent reference mc (log2 units) moves only when a row's maximum exceeds it by
-      // more than 8, so p <= 2^8 and the rescale of O^T and l is rare; exact either way, since
-      // l and O^T share the reference.
-      if (__any(tm > mc + 8.0f)) {
-        const float mn = fmaxf(mc, tm);
-        // 0 when mc = -inf (nothing accumulated yet), also for rows that still see no key
-        const float alpha = hw_exp2(mc - (mn == -INFINITY ? 0.f : mn));
-#pragma unroll
-        for (int j = 0; j < OB; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
-        l *= alpha;
-        mc = mn;
       }
-      const float mu = mc == -INFINITY ? 0.f : mc;
-      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      // Softmax with a lazy reference. The exact maximum is taken only while some row of the
+      // wave has no reference yet, or when the tile's sum of p exceeds 2^64 (a row's scores grew
+      // far past its reference); otherwise p = 2^(s c - mc) is used as is: l and O^T share mc,
+      // so the result is exact, and p <= 2^64 keeps every value finite. Values of p far below
+      // 1 stay normal floats (bf16 and float32 share the exponent range).
+      bool exact = __any(mc == -INFINITY);
+      float lt;
       bf16x8 pk[4];
+      for (int attempt = 0; attempt < 2; ++attempt) {
+        if (exact) {
+          float m4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            m4[u] = fmaxf(fmaxf(fmaxf(sacc[0][4 * u], sacc[0][4 * u + 1]), sacc[0][4 * u + 2]),
+                          fmaxf(fmaxf(sacc[0][4 * u + 3], sacc[1][4 * u]),
+                                fmaxf(sacc[1][4 * u + 1], fmaxf(sacc[1][4 * u + 2], sacc[1][4 * u + 3]))));
+          const float tm = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
+          const float mn = fmaxf(mc, tm);
+          // 0 when mc = -inf (nothing accumulated yet), also for rows that still see no key
+          const float alpha = hw_exp2(mc - (mn == -INFINITY ? 0.f : mn));
+#pragma unroll
+          for (int j = 0; j < OB; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
+          l *= alpha;
+          mc = mn;
+        }
+        const float mu = mc == -INFINITY ? 0.f : mc;
+        lt = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c, -mu));
+            const float p1 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e + 1], c, -mu));
+            const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+            lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);   // sum of the rounded p
+            pk[ks][e] = pp[0];
+            pk[ks][e + 1] = pp[1];
+          }
+        if (exact || !__any(!(lt <= 0x1p64f))) break;
+        exact = true;
+      }
+      l += lt;
+      // O^T += V^T P^T; k-step ks covers keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, and V^T is
+      // read in the same key order with the transposing LDS read
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = hw_exp2(fmaf(sc[8 * ks + e], c, -mu));
-          const float p1 = hw_exp2(fmaf(sc[8 * ks + e + 1], c, -mu));
-          const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);   // sum of the rounded p
-          pk[ks][e] = pp[0];
-          pk[ks][e + 1] = pp[1];
+        for (int j = 0; j < OB; ++j) {
+          const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][0]));
+          const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][1]));
+          const i16x4 both[2] = {vlo, vhi};
+          o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(both),
+                                                         pk[ks], o[j], 0, 0, 0);
         }
-      // O^T += V^T P^T; k-step ks = 2 kb + sub covers keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}
-#pragma unroll
-      for (int j = 0; j < OB; ++j)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j][ks], pk[ks], o[j], 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile t + 1 have landed
+    // this wave's copies of tile t + 1 have landed (later tiles may still fly) ...
+    if (t + kAhead < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kAhead - 1) * kLoadsPerTile));
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();                  // ... and every wave is done with tile t
   }
 
   // epilogue: combine the two key halves of every query, normalise, write O and LSE
-  const float lt = l + __shfl_xor(l, 32);
-  if (valid) {
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float lsum = half_sum(l);
+  if (i < s1) {
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     __bf16* orow = static_cast<__bf16*>(p.out) + i * hs + h * HD + 4 * hf;
 #pragma unroll
     for (int j = 0; j < OB; ++j)
@@ -324,7 +360,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
         *reinterpret_cast<bf16x4*>(orow + 32 * j + 8 * gq) = vv;
       }
     if (p.lse && hf == 0)
-      p.lse[static_cast<size_t>(h) * p.T + i] = lt > 0.f ? (mc + hw_log2(lt)) * kLn2 : -INFINITY;
+      p.lse[static_cast<size_t>(h) * p.T + i] = lsum > 0.f ? (mc + hw_log2(lsum)) * kLn2 : -INFINITY;
   }
 }
 
@@ -332,7 +368,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
 
 hipError_t launch_attn_mfma(const AttnParams& p, int hd, hipStream_t stream) {
   const int n_bh8 = ceil_div(p.S * p.H, 8) * 8;
-  dim3 grid(ceil_div(p.max_seqlen, BM) * n_bh8);
+  dim3 grid(ceil_div(p.max_seqlen, 128) * n_bh8);
   if (hd == 64) {
     hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(NT), 0, stream, p);
   } else {
