@@ -38,8 +38,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -91,11 +91,12 @@ def attention_pairs(seq_cu, chunk_cu_np, token_chunk_np, L, train) -> int:
     return total
 
 
-def cpu_baseline(cfg, inp, T_full):
-    """The oracle as it stands, on a bounded sample of the same workload: the scan over the
-    first 1024 tokens of sequence 0 (all channels, both SSMs) and the attention of (sequence
-    0, head 0) over all its rows; scaled to the whole batch (scan is linear in tokens,
-    attention in sequence-head pairs)."""
+def cpu_baseline(cfg, inp, T_full, scan_budget_s=3.0, attn_budget_s=8.0):
+    """The oracle as it stands, on a bounded sample of the same workload: the scan over a
+    whole-chunk prefix of sequence 0 (all channels, both SSMs; the prefix grows from 1024
+    tokens until about scan_budget_s of work) and the attention of sequence 0 for as many
+    heads as fit in about attn_budget_s; scaled to the whole batch (the scan is linear in
+    tokens, the attention in sequence-head pairs)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -105,30 +106,39 @@ def cpu_baseline(cfg, inp, T_full):
     f = {k: inp.f64(k) for k in list(inp.act) + list(inp.param)}
     chunk_cu, tc, ie = oracle.segment(inp.seq_cu, None if inp.chunk_lens is not None else cfg.P,
                                       cfg.layer_idx, inp.chunk_lens)
-    n_scan = min(1024, int(inp.seq_cu[1]))
-    n_scan = int(chunk_cu[np.searchsorted(chunk_cu, n_scan)])   # whole chunks
-    t0 = time.perf_counter()
-    for tag in ("k", "v"):
-        oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
-                              f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"], chunk_cu,
-                              t_begin=0, t_end=n_scan)
-    t_scan = time.perf_counter() - t0
     s0, s1 = int(inp.seq_cu[0]), int(inp.seq_cu[1])
+
+    def scan_prefix(n_tok):
+        n_tok = int(chunk_cu[np.searchsorted(chunk_cu, min(n_tok, s1))])   # whole chunks
+        t0 = time.perf_counter()
+        for tag in ("k", "v"):
+            oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
+                                  f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"], chunk_cu,
+                                  t_begin=0, t_end=n_tok)
+        return n_tok, time.perf_counter() - t0
+
+    n_scan, t_scan = scan_prefix(1024)
+    if t_scan < scan_budget_s and n_scan < s1:
+        n_scan, t_scan = scan_prefix(int(n_scan * scan_budget_s / max(t_scan, 1e-3)))
     H, hd = cfg.H, cfg.hd
-    q = f["q"][s0:s1].reshape(-1, H, hd)[:, :1]
     rng = np.random.default_rng(0)
-    k = rng.standard_normal((s1 - s0, 1, hd))
-    v = rng.standard_normal((s1 - s0, 1, hd))
-    t0 = time.perf_counter()
-    oracle.chunk_attention(q, k, v, [0, s1 - s0], tc[s0:s1] - tc[s0], ie[s0:s1], cfg.L, cfg.mode)
-    t_attn = time.perf_counter() - t0
+    t_attn, heads = 0.0, 0
+    while heads < H and t_attn < attn_budget_s:
+        q = f["q"][s0:s1].reshape(-1, H, hd)[:, heads:heads + 1]
+        k = rng.standard_normal((s1 - s0, 1, hd))
+        v = rng.standard_normal((s1 - s0, 1, hd))
+        t0 = time.perf_counter()
+        oracle.chunk_attention(q, k, v, [0, s1 - s0], tc[s0:s1] - tc[s0], ie[s0:s1], cfg.L,
+                               cfg.mode)
+        t_attn += time.perf_counter() - t0
+        heads += 1
     n_pairs = (len(inp.seq_cu) - 1) * H
-    est = t_scan * (T_full / n_scan) + t_attn * n_pairs
+    est = t_scan * (T_full / n_scan) + t_attn / heads * n_pairs
     return {"value": T_full / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": (f"oracle scan of tokens 0..{n_scan - 1} of sequence 0 (all {cfg.d} channels, "
-                       f"both SSMs: {t_scan:.2f} s) scaled by {T_full / n_scan:.1f}; oracle attention of "
-                       f"sequence 0, head 0 ({s1 - s0} rows: {t_attn:.2f} s) scaled by {n_pairs} "
-                       f"sequence-head pairs; estimated {est:.1f} s per step")}
+                       f"both SSMs: {t_scan:.2f} s) scaled by {T_full / n_scan:.2f}; oracle attention of "
+                       f"sequence 0, heads 0..{heads - 1} ({s1 - s0} rows each: {t_attn:.2f} s) scaled "
+                       f"to {n_pairs} sequence-head pairs; estimated {est:.1f} s per step")}
 
 
 def bench_prefill(args):
@@ -218,6 +228,7 @@ def bench_prefill(args):
     scan_alu_tslots = scan_slots / (scan_ms * 1e-3) / 1e12
     alu_peak = VALU_SLOTS_PER_S / 1e12
     traffic = measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"])
+    attn_traffic = measured_traffic("attn_mfma_kernel", ["attn_mfma.hip", "common.h"])
     roofline = {"bound": "alu", "kernel": "kvssm_scan_kernel", "achieved": round(scan_alu_tslots, 3),
                 "peak": round(alu_peak, 3), "unit": "T VALU-slot/s", "frac": round(scan_alu_tslots / alu_peak, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
@@ -239,7 +250,8 @@ def bench_prefill(args):
                      "frac_of_8TBps": round(scan_gbps / HBM_PEAK_GBPS, 4)},
         "attn_mfma": {"algorithmic_flop": attn_flop, "visible_pairs_per_head": pairs,
                       "TFLOPs": round(attn_tflops, 2),
-                      "frac_of_2.5PF": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+                      "frac_of_2.5PF": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "traffic": None if attn_traffic is None else attn_traffic["bytes_per_launch"]},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, T)
