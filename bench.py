@@ -27,11 +27,13 @@ if ROOT not in sys.path:
 METRIC = "tokens/sec fwd (KV-SSM scan+chunk attn); scan HBM GB/s %peak; attn MFMA %"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-# VALU issue capacity: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-instruction slots per second.
-VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
-# Minimal VALU issue slots per state update of the scan: multiply for the exponent, v_exp_f32
-# (half rate on gfx950: 2 slots), multiply for the input term, FMA state, FMA output.
-SLOTS_PER_UPDATE = 6
+# VALU issue capacity: 256 CUs x 4 SIMDs x 32 fp32 lanes per clock x 2.4 GHz = 78.6 T
+# lane-instruction slots per second (the 157.3 TFLOP/s fp32 vector peak counts an FMA as two).
+VALU_SLOTS_PER_S = 256 * 4 * 32 * 2.4e9
+# VALU issue slots per state update of the scan: multiply for the exponent, v_exp_f32, multiply
+# for the input term, FMA state, FMA output. A wave64 v_exp_f32 occupies the SIMD 2.75 times as
+# long as a wave64 FMA (5.5 vs 2.0 clocks, measured at 4 waves per SIMD), so it counts 2.75.
+SLOTS_PER_UPDATE = 6.75
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

@@ -88,6 +88,30 @@ __device__ __forceinline__ int tile_off(int r, int e) {
   return r * HD + 8 * ((e >> 3) ^ swz<HD>(r)) + (e & 7);
 }
 
+// p = 2^(s c - mu) for the 32 scores of this lane, rounded to bf16 and packed as the P^T
+// operand of the second product (k-step ks: keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, in the
+// accumulator's row order); returns the lane's sum of the rounded p.
+__device__ __forceinline__ float tile_exp(const f32x16 (&sacc)[2], float c, float mu,
+                                          bf16x8 (&pk)[4]) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float lt = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c, -mu));
+      const float p1 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e + 1], c, -mu));
+      const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+      lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
+      w[e >> 1] = __builtin_bit_cast(unsigned, pp);
+    }
+    pk[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+  return lt;
+}
+
 #ifndef ATTN_NBUF
 #define ATTN_NBUF 2
 #endif
@@ -227,7 +251,6 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   else __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   const f32x16 zero16 = {};
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t % NBUF;
@@ -287,43 +310,31 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
       // far past its reference); otherwise p = 2^(s c - mc) is used as is: l and O^T share mc,
       // so the result is exact, and p <= 2^64 keeps every value finite. Values of p far below
       // 1 stay normal floats (bf16 and float32 share the exponent range).
-      bool exact = __any(mc == -INFINITY);
-      float lt;
       bf16x8 pk[4];
-      for (int attempt = 0; attempt < 2; ++attempt) {
-        if (exact) {
-          float m4[4];
+      float lt = 0.f;
+      bool exact = __any(mc == -INFINITY);
+      if (!exact) {
+        lt = tile_exp(sacc, c, mc, pk);
+        exact = __any(!(lt <= 0x1p64f));
+      }
+      if (exact) {
+        float m4[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            m4[u] = fmaxf(fmaxf(fmaxf(sacc[0][4 * u], sacc[0][4 * u + 1]), sacc[0][4 * u + 2]),
-                          fmaxf(fmaxf(sacc[0][4 * u + 3], sacc[1][4 * u]),
-                                fmaxf(sacc[1][4 * u + 1], fmaxf(sacc[1][4 * u + 2], sacc[1][4 * u + 3]))));
-          const float tm = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
-          const float mn = fmaxf(mc, tm);
-          // 0 when mc = -inf (nothing accumulated yet), also for rows that still see no key
-          const float alpha = hw_exp2(mc - (mn == -INFINITY ? 0.f : mn));
+        for (int u = 0; u < 4; ++u)
+          m4[u] = fmaxf(fmaxf(fmaxf(sacc[0][4 * u], sacc[0][4 * u + 1]), sacc[0][4 * u + 2]),
+                        fmaxf(fmaxf(sacc[0][4 * u + 3], sacc[1][4 * u]),
+                              fmaxf(sacc[1][4 * u + 1], fmaxf(sacc[1][4 * u + 2], sacc[1][4 * u + 3]))));
+        const float tm = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
+        const float mn = fmaxf(mc, tm);
+        // 0 when mc = -inf (nothing accumulated yet), also for rows that still see no key
+        const float alpha = hw_exp2(mc - (mn == -INFINITY ? 0.f : mn));
 #pragma unroll
-          for (int j = 0; j < OB; ++j)
+        for (int j = 0; j < OB; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
-          l *= alpha;
-          mc = mn;
-        }
-        const float mu = mc == -INFINITY ? 0.f : mc;
-        lt = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c, -mu));
-            const float p1 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e + 1], c, -mu));
-            const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
-            lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);   // sum of the rounded p
-            pk[ks][e] = pp[0];
-            pk[ks][e + 1] = pp[1];
-          }
-        if (exact || !__any(!(lt <= 0x1p64f))) break;
-        exact = true;
+          for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
+        l *= alpha;
+        mc = mn;
+        lt = tile_exp(sacc, c, mc == -INFINITY ? 0.f : mc, pk);
       }
       l += lt;
       // O^T += V^T P^T; k-step ks covers keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, and V^T is

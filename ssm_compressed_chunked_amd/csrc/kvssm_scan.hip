@@ -57,6 +57,7 @@ struct SsmLane {
   }
 
   // One token. FIRST: the state restarts (no decay term). bm/cm point at the token's rows.
+  // The output sum runs in two halves to shorten its dependency chain.
   template <bool FIRST>
   __device__ __forceinline__ float step(float x, float dt, const T* __restrict__ bm,
                                         const T* __restrict__ cm) {
@@ -65,7 +66,7 @@ struct SsmLane {
     load_row(cm, cc);
     const float delta = softplus_f32(dt + bias);
     const float u = delta * x;
-    float y = 0.0f;
+    float y0 = 0.0f, y1 = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       const float inj = u * b[n];
@@ -74,9 +75,10 @@ struct SsmLane {
       } else {
         h[n] = fmaf(hw_exp2(delta * A2[n]), h[n], inj);
       }
-      y = fmaf(h[n], cc[n], y);
+      if (n & 1) y1 = fmaf(h[n], cc[n], y1);
+      else y0 = fmaf(h[n], cc[n], y0);
     }
-    return fmaf(D, x, y);
+    return fmaf(D, x, y0 + y1);
   }
 
   // A wave-uniform row of N values, read as 32-bit words so that the compiler issues scalar
