@@ -129,27 +129,53 @@ __host__ __device__ constexpr int vmcnt_at_most(int n) {
   return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
 }
 
-// Issue the LDS-direct copies of one tile (keys base .. base + BN - 1; keys past `top`, the last
-// valid key, re-read row `top`: every row that could see such a key masks it). Each wave copies
-// NI chunks of 1 KB; lane l of chunk ch fills 16-byte slot ch * 64 + l of the tile.
+// The LDS-direct copies of one tile. Each wave copies NI chunks of 1 KB; lane l of chunk ch
+// fills 16-byte slot ch * 64 + l of the tile, which holds segment pos of tile row r (slot =
+// r * SPR + (pos ^ swz(r))). The per-lane part of the source address, r * hs + 8 * seg, does not
+// depend on the tile and is computed once.
 template <int HD>
-__device__ __forceinline__ void tile_issue(__bf16* sk, __bf16* sv, const __bf16* kp,
-                                           const __bf16* vp, int base, int top, int hs, int wid,
-                                           int lane) {
-  constexpr int SPR = HD / 8;                    // 16-byte segments per row
-  constexpr int NI = BN * SPR / kWave / 4;       // 1 KB chunks per wave
+struct TileCopy {
+  static constexpr int SPR = HD / 8;                    // 16-byte segments per row
+  static constexpr int NI = BN * SPR / kWave / 4;       // 1 KB chunks per wave
+  int off[NI];   // element offset of this lane's segment from the tile's first key row
+  int row[NI];   // its tile row
+  int seg8[NI];  // its element offset within the row
+
+  __device__ __forceinline__ void init(int wid, int lane, int hs) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int ch = wid * NI + i;
-    const int slot = ch * kWave + lane;
-    const int r = slot / SPR, pos = slot % SPR;
-    const int seg = pos ^ swz<HD>(r);
-    const int key = min(base + r, top);
-    const int go = key * hs + seg * 8;
-    __builtin_amdgcn_global_load_lds(kp + go, LDS_PTR(void, sk + ch * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + go, LDS_PTR(void, sv + ch * 512), 16, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      const int slot = (wid * NI + i) * kWave + lane;
+      const int r = slot / SPR, pos = slot % SPR;
+      row[i] = r;
+      seg8[i] = 8 * (pos ^ swz<HD>(r));
+      off[i] = r * hs + seg8[i];
+    }
   }
-}
+  // keys base .. base + BN - 1; keys past `top`, the last valid key, re-read row `top` (every
+  // row that could see such a key masks it). base, top and wid are wave-uniform.
+  __device__ __forceinline__ void issue(__bf16* sk, __bf16* sv, const __bf16* kp,
+                                        const __bf16* vp, int base, int top, int hs,
+                                        int wid) const {
+    if (base + BN - 1 <= top) {
+      const __bf16* kt = kp + static_cast<size_t>(base) * hs;
+      const __bf16* vt = vp + static_cast<size_t>(base) * hs;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int ch = wid * NI + i;
+        __builtin_amdgcn_global_load_lds(kt + off[i], LDS_PTR(void, sk + ch * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + off[i], LDS_PTR(void, sv + ch * 512), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int ch = wid * NI + i;
+        const int go = min(base + row[i], top) * hs + seg8[i];
+        __builtin_amdgcn_global_load_lds(kp + go, LDS_PTR(void, sk + ch * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + go, LDS_PTR(void, sv + ch * 512), 16, 0, 0);
+      }
+    }
+  }
+};
 
 template <int HD>
 __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
@@ -171,7 +197,8 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const int s0 = p.seq_cu[s], s1 = p.seq_cu[s + 1];
   const int r0 = s0 + qt * BM;
   if (r0 >= s1) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane & 31, hf = lane >> 5;
   const int last = min(r0 + BM, s1) - 1;
   const int c0 = p.token_chunk[s0];
@@ -182,8 +209,10 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const int ic = min(i, last);
   const Geo g = geo(p, ic, s0, s1, c0);
   const int wr0 = min(r0 + wid * 32, last), wr1 = min(r0 + wid * 32 + 31, last);
-  const int Ew0 = __shfl(g.E, 0), Ew1 = __shfl(g.E, 31);
-  const int ww0 = __shfl(g.w, 0), ww1 = __shfl(g.w, 31);
+  const int Ew0 = __builtin_amdgcn_readfirstlane(__shfl(g.E, 0));
+  const int Ew1 = __builtin_amdgcn_readfirstlane(__shfl(g.E, 31));
+  const int ww0 = __builtin_amdgcn_readfirstlane(__shfl(g.w, 0));
+  const int ww1 = __builtin_amdgcn_readfirstlane(__shfl(g.w, 31));
   // the workgroup's key ranges
   const Geo gl = geo(p, last, s0, s1, c0);
   const Geo gf = geo(p, r0, s0, s1, c0);
@@ -236,13 +265,15 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
         }
   }
 
+  TileCopy<HD> tc;
+  tc.init(wid, lane, hs);
   auto issue = [&](int t) {
     const bool bt = t < nbt;
     const int buf = t % NBUF;
-    tile_issue<HD>(sm.k[buf], sm.v[buf], bt ? kbp : ktp, bt ? vbp : vtp,
-                   bt ? c0 + t * BN : band0 + (t - nbt) * BN, bt ? topb : last, hs, wid, lane);
+    tc.issue(sm.k[buf], sm.v[buf], bt ? kbp : ktp, bt ? vbp : vtp,
+             bt ? c0 + t * BN : band0 + (t - nbt) * BN, bt ? topb : last, hs, wid);
   };
-  constexpr int kLoadsPerTile = 2 * (BN * (HD / 8) / kWave / 4);   // per wave
+  constexpr int kLoadsPerTile = 2 * TileCopy<HD>::NI;               // per wave
   constexpr int kAhead = NBUF - 1;                                 // tiles in flight
 #pragma unroll
   for (int a = 0; a < kAhead; ++a)
@@ -287,18 +318,26 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
         }
       } else {
         const int kbase = base + 4 * hf;
-        // visible iff lo <= C <= hi (boundary tiles: below c0 + E; band tiles: w .. i)
-        const int lo = bnd ? -(1 << 30) : g.w - kbase;
+        // visible iff lo <= C <= hi (boundary tiles: C <= hi, below c0 + E; band tiles: w .. i)
+        const int lo = g.w - kbase;
         const int hi = bnd ? c0 + g.E - 1 - kbase : ic - kbase;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           bf16x8 ka[QS];
 #pragma unroll
           for (int st = 0; st < QS; ++st) ka[st] = *reinterpret_cast<const bf16x8*>(sk + koff[kb][st]);
+          if (bnd) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
-            sacc[kb][v] = (C >= lo && C <= hi) ? 0.f : -INFINITY;
+            for (int v = 0; v < 16; ++v) {
+              const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
+              sacc[kb][v] = C <= hi ? 0.f : -INFINITY;
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
+              sacc[kb][v] = (C >= lo && C <= hi) ? 0.f : -INFINITY;
+            }
           }
 #pragma unroll
           for (int st = 0; st < QS; ++st)
