@@ -89,7 +89,7 @@ int attamba_chunk_cu_from_lengths(const int32_t* seq_cu_host, int32_t S,
                                   int32_t* chunk_cu_host_out);
 
 /* Device. Uniform chunking computed on the GPU from the device copy of seq_cu[S+1] over
- * T tokens. Writes chunk_cu[n_chunks + 1] (chunk start offsets, then T), and, if not NULL,
+ * T tokens (seq_cu[0] = 0, non-decreasing, seq_cu[S] = T). Writes chunk_cu[n_chunks + 1] (chunk start offsets, then T), and, if not NULL,
  * token_chunk[T] (chunk of every token) and is_end[T] (1 at the last token of every chunk,
  * else 0). n_chunks must be the count attamba_count_chunks returns for the same seq_cu; the
  * kernels never write past n_chunks + 1 entries. Errors: NULL_ARG (seq_cu, chunk_cu),

@@ -69,16 +69,30 @@ def test_uniform_boundaries_bit_exact(seq_lens, P, layer):
     np.testing.assert_array_equal(lay.is_end.cpu().numpy(), ref_ie)
 
 
-def test_many_sequences_boundaries():
-    rng = np.random.default_rng(5)
-    lens = rng.integers(0, 40, size=3000)
+@pytest.mark.parametrize("n_seq,P,layer", [(3000, 6, 4), (4096, 3, 1), (4097, 7, 0), (6000, 5, 2)])
+def test_many_sequences_boundaries(n_seq, P, layer):
+    """Batches up to 4096 sequences take the one-launch layout kernel, larger ones the
+    two-kernel path; empty sequences included."""
+    say(f"boundaries n_seq={n_seq} P={P} layer={layer}")
+    rng = np.random.default_rng(5 + n_seq)
+    lens = rng.integers(0, 40, size=n_seq)
+    lens[0] = 0
     seq_cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(seq_cu_h[-1])
-    lay = chunk_layout(seq_cu_h, torch.from_numpy(seq_cu_h).cuda(), T, 6, 4)
-    ref_cu, ref_tc, ref_ie = oracle.segment(seq_cu_h, 6, 4)
+    lay = chunk_layout(seq_cu_h, torch.from_numpy(seq_cu_h).cuda(), T, P, layer)
+    ref_cu, ref_tc, ref_ie = oracle.segment(seq_cu_h, P, layer)
     np.testing.assert_array_equal(lay.chunk_cu.cpu().numpy(), ref_cu)
     np.testing.assert_array_equal(lay.token_chunk.cpu().numpy(), ref_tc)
     np.testing.assert_array_equal(lay.is_end.cpu().numpy(), ref_ie)
+
+
+def test_empty_batch_boundaries():
+    """All sequences empty: no chunks, chunk_cu = [0]."""
+    seq_cu_h = np.zeros(4, dtype=np.int32)
+    lay = chunk_layout(seq_cu_h, torch.from_numpy(seq_cu_h).cuda(), 0, 4, 1)
+    assert lay.n_chunks == 0
+    np.testing.assert_array_equal(lay.chunk_cu.cpu().numpy(), [0])
+    assert lay.token_chunk.numel() == 0 and lay.is_end.numel() == 0
 
 
 def test_random_chunk_index_bit_exact():
