@@ -225,6 +225,7 @@ int attamba_decode_step(attamba_decode_cache* c, const attamba_decode_inputs* in
   dl.n_bound_before = c->n_bound;
   const int64_t w = c->L > 0 ? (pos - c->L + 1 > 0 ? pos - c->L + 1 : 0) : pos + 1;
   dl.w = static_cast<int>(w);
+  dl.w_slot = c->L > 0 ? static_cast<int>(w % c->L) : 0;
   dl.E = static_cast<int>(ends_before(w, P, o));
   dl.n_window = c->L > 0 ? static_cast<int>(pos - w + 1) : 0;
   dl.scale = 1.0f / std::sqrt(static_cast<float>(c->hd));

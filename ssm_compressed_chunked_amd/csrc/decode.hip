@@ -3,7 +3,7 @@
 // boundary states are cached; "If this is right": the cache shrinks by about P).
 //
 // Three launches on the caller's stream:
-//   1. decode_update: one lane per (sequence, channel): zero the state at a chunk start, one
+//   1. decode_update: four lanes per (sequence, channel): zero the state at a chunk start, one
 //      SSM_K and SSM_V step, write the token's key/value into its window slot and, at a chunk
 //      end, append it as the next boundary state;
 //   2. decode_attn_split: the key list of each (sequence, head) — boundary states 0..E-1 then
@@ -20,38 +20,68 @@ namespace {
 
 constexpr int kSplit = 256;          // keys per split workgroup
 constexpr int kSplitThreads = 256;
+constexpr int kUpdLanes = 4;         // lanes per (sequence, channel) in the state update
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// VEC consecutive elements of a 16-byte word as float
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack16(const u32x4& w, float (&f)[VEC]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+
+// One SSM_K and SSM_V step per (sequence, channel); the N states of a channel are spread over
+// kUpdLanes consecutive lanes (NQ each), whose partial outputs meet with two lane swaps.
 template <typename T, int N>
-__global__ __launch_bounds__(kWave) void decode_update_kernel(attamba_decode_cache c,
-                                                              attamba_decode_inputs in,
-                                                              DecodeLaunch dl) {
+__global__ __launch_bounds__(256) void decode_update_kernel(attamba_decode_cache c,
+                                                            attamba_decode_inputs in,
+                                                            DecodeLaunch dl) {
+  constexpr int NQ = N / kUpdLanes;
   const int b = blockIdx.y;
-  const int ch = blockIdx.x * kWave + threadIdx.x;
+  const int ch = blockIdx.x * (256 / kUpdLanes) + threadIdx.x / kUpdLanes;
+  const int part = threadIdx.x % kUpdLanes;
   const int d = c.d;
   const size_t bd = static_cast<size_t>(b) * d + ch;
   const float x = to_f32(static_cast<const T*>(in.x)[bd]);
   const int head = ch / c.hd, e = ch % c.hd;
   auto run = [&](const float* A, const float* D, const float* bias, const T* dt, const T* bm,
                  const T* cm, float* hstate) -> float {
+    float a[NQ], hp[NQ], bv[NQ], cv[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      a[n] = A[static_cast<size_t>(ch) * N + part * NQ + n];
+      hp[n] = hstate[bd * N + part * NQ + n];
+      bv[n] = to_f32(bm[static_cast<size_t>(b) * N + part * NQ + n]);
+      cv[n] = to_f32(cm[static_cast<size_t>(b) * N + part * NQ + n]);
+    }
     const float delta = softplus_f32(to_f32(dt[bd]) + bias[ch]);
     const float u = delta * x;
-    float* hp = hstate + bd * N;
-    const T* bmr = bm + static_cast<size_t>(b) * N;
-    const T* cmr = cm + static_cast<size_t>(b) * N;
     float y = 0.f;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      const float inj = u * to_f32(bmr[n]);
-      const float hn = dl.is_start ? inj : fmaf(hw_exp2(delta * A[ch * N + n] * kLog2e), hp[n], inj);
-      hp[n] = hn;
-      y = fmaf(hn, to_f32(cmr[n]), y);
+    for (int n = 0; n < NQ; ++n) {
+      const float inj = u * bv[n];
+      const float hn = dl.is_start ? inj : fmaf(hw_exp2(delta * a[n] * kLog2e), hp[n], inj);
+      hstate[bd * N + part * NQ + n] = hn;
+      y = fmaf(hn, cv[n], y);
     }
+    y += __shfl_xor(y, 1, kWave);
+    y += __shfl_xor(y, 2, kWave);
     return fmaf(D[ch], x, y);
   };
   const float yk = run(c.A_k, c.D_k, c.bias_k, static_cast<const T*>(in.dt_k),
                        static_cast<const T*>(in.bm_k), static_cast<const T*>(in.cm_k), c.h_k);
   const float yv = run(c.A_v, c.D_v, c.bias_v, static_cast<const T*>(in.dt_v),
                        static_cast<const T*>(in.bm_v), static_cast<const T*>(in.cm_v), c.h_v);
+  if (part != 0) return;
   const size_t bh = static_cast<size_t>(b) * c.H + head;
   if (c.L > 0) {
     const size_t o = (bh * c.L + dl.slot) * c.hd + e;
@@ -65,19 +95,23 @@ __global__ __launch_bounds__(kWave) void decode_update_kernel(attamba_decode_cac
   }
 }
 
-// Row pointer of key k of (b, h): boundary state k < E, else window position w + (k - E).
-template <typename T>
-__device__ __forceinline__ size_t key_row(const attamba_decode_cache& c, const DecodeLaunch& dl,
+// Element offset of key k of (b, h): boundary state k < E, else window position
+// w + (k - E), held in ring slot (w mod L + k - E) mod L.
+__device__ __forceinline__ size_t key_off(const attamba_decode_cache& c, const DecodeLaunch& dl,
                                           size_t bh, int k, bool& in_window) {
   if (k < dl.E) {
     in_window = false;
     return (bh * c.cap + k) * c.hd;
   }
   in_window = true;
-  const int64_t pos = dl.w + (k - dl.E);
-  return (bh * c.L + static_cast<int>(pos % c.L)) * c.hd;
+  int sl = dl.w_slot + (k - dl.E);
+  if (sl >= c.L) sl -= c.L;
+  return (bh * c.L + sl) * c.hd;
 }
 
+// One split of kSplit keys of one (sequence, head). A key row is read by LPK lanes with 16-byte
+// loads (KPW rows per wave instruction); the loads of NB rows per lane are issued together
+// before any is used, for both the K pass (scores) and the V pass (P V).
 template <typename T, int HD>
 __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
     attamba_decode_cache c, attamba_decode_inputs in, DecodeLaunch dl, int max_splits) {
@@ -86,6 +120,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   constexpr int KPW = kWave / LPK;             // key rows per wave instruction
   constexpr int NW = kSplitThreads / kWave;
   constexpr int KPB = KPW * NW;                // key rows per workgroup iteration
+  constexpr int NIT = kSplit / KPB;            // iterations per split
+  constexpr int NB = NIT < 8 ? NIT : 8;        // iterations whose loads fly together
   __shared__ float s_p[kSplit];
   __shared__ float s_red[NW];
   __shared__ float s_acc[NW][KPW][HD];
@@ -98,6 +134,11 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   const int k0 = sp * kSplit;
   const int nk = min(kSplit, n_keys - k0);
   float* part = static_cast<float*>(c.workspace) + (bh * max_splits + sp) * (HD + 2);
+  if (nk <= 0) {   // no key in this split (only when the whole list is empty)
+    for (int e = tid; e < HD; e += kSplitThreads) part[e] = 0.f;
+    if (tid == 0) { part[HD] = -INFINITY; part[HD + 1] = 0.f; }
+    return;
+  }
 
   float qv[VEC];
   {
@@ -112,18 +153,28 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   const T* vwin = static_cast<const T*>(c.vw);
 
   // scores (log2 units)
-  for (int kk = wid * KPW + grp; kk < KPB * ceil_div(nk, KPB); kk += KPB) {
-    float sc = 0.f;
-    if (kk < nk) {
-      bool win;
-      const size_t row = key_row<T>(c, dl, bh, k0 + kk, win);
-      const T* kr = (win ? kwin : kbase) + row + sub * VEC;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) sc = fmaf(qv[v], to_f32(kr[v]), sc);
+  for (int i0 = 0; i0 < NIT; i0 += NB) {
+    u32x4 raw[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int kk = min((i0 + u) * KPB + wid * KPW + grp, nk - 1);
+      bool win;
+      const size_t off = key_off(c, dl, bh, k0 + kk, win);
+      raw[u] = *reinterpret_cast<const u32x4*>((win ? kwin : kbase) + off + sub * VEC);
     }
 #pragma unroll
-    for (int off = 1; off < LPK; off <<= 1) sc += __shfl_xor(sc, off, kWave);
-    if (sub == 0 && kk < nk) s_p[kk] = sc;
+    for (int u = 0; u < NB; ++u) {
+      const int kk = (i0 + u) * KPB + wid * KPW + grp;
+      float kf[VEC];
+      unpack16<T, VEC>(raw[u], kf);
+      float sc = 0.f;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) sc = fmaf(qv[v], kf[v], sc);
+#pragma unroll
+      for (int off = 1; off < LPK; off <<= 1) sc += __shfl_xor(sc, off, kWave);
+      if (sub == 0 && kk < nk) s_p[kk] = sc;
+    }
   }
   __syncthreads();
   // max over the split
@@ -137,25 +188,36 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_red[w]);
   __syncthreads();
   float sum = 0.f;
-  for (int k = tid; k < nk; k += kSplitThreads) {
-    const float pr = hw_exp2(s_p[k] - mx);
+  for (int k = tid; k < kSplit; k += kSplitThreads) {
+    const float pr = k < nk ? hw_exp2(s_p[k] - mx) : 0.f;
     s_p[k] = pr;
     sum += pr;
   }
   for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
   if (lane == 0) s_red[wid] = sum;
   __syncthreads();
-  // P V
+  // P V (rows past nk re-read the last key with weight 0)
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-  for (int kk = wid * KPW + grp; kk < nk; kk += KPB) {
-    bool win;
-    const size_t row = key_row<T>(c, dl, bh, k0 + kk, win);
-    const T* vr = (win ? vwin : vbase) + row + sub * VEC;
-    const float pr = s_p[kk];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = fmaf(pr, to_f32(vr[v]), acc[v]);
+  for (int i0 = 0; i0 < NIT; i0 += NB) {
+    u32x4 raw[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int kk = min((i0 + u) * KPB + wid * KPW + grp, nk - 1);
+      bool win;
+      const size_t off = key_off(c, dl, bh, k0 + kk, win);
+      raw[u] = *reinterpret_cast<const u32x4*>((win ? vwin : vbase) + off + sub * VEC);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float pr = s_p[(i0 + u) * KPB + wid * KPW + grp];
+      float vf[VEC];
+      unpack16<T, VEC>(raw[u], vf);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] = fmaf(pr, vf[v], acc[v]);
+    }
   }
 #pragma unroll
   for (int v = 0; v < VEC; ++v) s_acc[wid][grp][sub * VEC + v] = acc[v];
@@ -169,23 +231,35 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   if (tid == 0) {
     float l = 0.f;
     for (int w = 0; w < NW; ++w) l += s_red[w];
-    part[HD] = nk > 0 ? mx : -INFINITY;
+    part[HD] = mx;
     part[HD + 1] = l;
   }
 }
 
+// Merges the split partials of one (sequence, head): thread e owns output element e.
 template <typename T, int HD>
 __global__ __launch_bounds__(HD) void decode_combine_kernel(attamba_decode_cache c,
                                                             attamba_decode_inputs in,
                                                             DecodeLaunch dl, int max_splits) {
+  constexpr int NWC = (HD + kWave - 1) / kWave;
+  __shared__ float s_red[NWC];
   const int h = blockIdx.x, b = blockIdx.y, e = threadIdx.x;
   const size_t bh = static_cast<size_t>(b) * c.H + h;
   const float* part = static_cast<const float*>(c.workspace) + bh * max_splits * (HD + 2);
+  const int ns = dl.n_splits;
   float mx = -INFINITY;
-  for (int s = 0; s < dl.n_splits; ++s) mx = fmaxf(mx, part[s * (HD + 2) + HD]);
+  for (int s = e; s < ns; s += HD) mx = fmaxf(mx, part[s * (HD + 2) + HD]);
+  for (int off = (HD < kWave ? HD : kWave) / 2; off > 0; off >>= 1)
+    mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+  if (e % kWave == 0) s_red[e / kWave] = mx;
+  __syncthreads();
+  mx = s_red[0];
+#pragma unroll
+  for (int w = 1; w < NWC; ++w) mx = fmaxf(mx, s_red[w]);
   float o = 0.f, l = 0.f;
   if (mx > -INFINITY) {
-    for (int s = 0; s < dl.n_splits; ++s) {
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) {
       const float* ps = part + s * (HD + 2);
       const float wgt = hw_exp2(ps[HD] - mx);
       o = fmaf(ps[e], wgt, o);
@@ -199,8 +273,8 @@ template <typename T, int N, int HD>
 hipError_t launch_typed(const attamba_decode_cache& c, const attamba_decode_inputs& in,
                         const DecodeLaunch& dl, hipStream_t stream) {
   const int max_splits = decode_max_splits(c.cap, c.L);
-  hipLaunchKernelGGL((decode_update_kernel<T, N>), dim3(c.d / kWave, c.B), dim3(kWave), 0, stream,
-                     c, in, dl);
+  hipLaunchKernelGGL((decode_update_kernel<T, N>), dim3(c.d * kUpdLanes / 256, c.B), dim3(256), 0,
+                     stream, c, in, dl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_attn_split_kernel<T, HD>), dim3(dl.n_splits, c.H, c.B),

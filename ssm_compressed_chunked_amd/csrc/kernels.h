@@ -34,6 +34,7 @@ struct DecodeLaunch {
   int E;                  // boundary states attended (chunk ends before the window)
   int n_window;           // window positions attended (pos - w + 1, or 0 if L = 0)
   int w;                  // first window position
+  int w_slot;             // its window slot, w mod L (L > 0)
   int n_splits;
   float scale;
 };
