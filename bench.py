@@ -7,6 +7,7 @@ N=16, P=8, L=64, uniform chunks, M_test + window). Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload prefill_bf16|varchunk_bf16|train_bf16]
     python bench.py --workload decode_bf16      # decode configuration, separate line
+    python bench.py --workload copy             # reference bandwidth (512 MiB device copy)
 """
 from __future__ import annotations
 
@@ -305,14 +306,18 @@ def bench_decode(args):
     kv_bytes = keys * cfg.B * cfg.H * cfg.hd * 2 * e
     state_bytes = cfg.steps * 2 * 2 * cfg.B * cfg.d * cfg.N * 4
     gbps = (kv_bytes + state_bytes) / wall / 1e9
+    traffic = measured_traffic("decode_step", ["decode.hip", "common.h"])
     line = {"metric": "decode tokens/s (boundary-state cache)", "value": round(cfg.B * cfg.steps / wall, 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": cfg.steps, "warmup": args.warmup,
             "ms_per_step": round(wall * 1e3 / cfg.steps, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
             "config": {"workload": cfg.name, "B": cfg.B, "ctx": cfg.ctx, "d_model": cfg.d,
                        "heads": cfg.H, "head_dim": cfg.hd, "N": cfg.N, "P": cfg.P, "L": cfg.L},
-            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
+            "roofline": {"bound": "hbm", "kernel": "decode step (update + split attention + combine)",
+                         "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                         "algorithmic_bytes_per_step": round((kv_bytes + state_bytes) / cfg.steps)}}
     print(json.dumps(line), flush=True)
 
 
