@@ -177,6 +177,47 @@ struct TileCopy {
   }
 };
 
+// S^T = K Q^T for one tile (keys on accumulator rows, this lane's query on its column). The mask
+// enters as the initial accumulator: 0 for a visible key, -inf for a hidden one (accumulator
+// row v of block kb is key base + 4 hf + C(kb, v), C = 32 kb + 8 (v / 4) + v % 4); fully
+// visible tiles start from the zero accumulator. Visible: lo <= C <= hi (boundary tiles only
+// test hi). koff: this lane's operand offsets for key block 0; block 1 lies 32 rows further
+// (the swizzle repeats every 16 rows).
+template <int HD, int QS>
+__device__ __forceinline__ void tile_scores(f32x16 (&sacc)[2], const __bf16* sk,
+                                            const int (&koff)[QS], const bf16x8 (&qf)[QS],
+                                            bool full, bool bnd, int lo, int hi) {
+  const f32x16 zero16 = {};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    bf16x8 ka[QS];
+#pragma unroll
+    for (int st = 0; st < QS; ++st)
+      ka[st] = *reinterpret_cast<const bf16x8*>(sk + koff[st] + 32 * HD * kb);
+    if (full) {
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], zero16, 0, 0, 0);
+    } else {
+      if (bnd) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
+          sacc[kb][v] = C <= hi ? 0.f : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
+          sacc[kb][v] = (C >= lo && C <= hi) ? 0.f : -INFINITY;
+        }
+      }
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], sacc[kb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int st = 1; st < QS; ++st)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], sacc[kb], 0, 0, 0);
+  }
+}
+
 template <int HD>
 __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   constexpr int QS = HD / 16;     // k-steps of S^T (16 hd each)
@@ -245,24 +286,17 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const __bf16* vtp = static_cast<const __bf16*>(p.v) + h * HD;
 
   // per-lane LDS element offsets that do not depend on the tile
-  int koff[2][QS];                 // S^T operand: row 32 kb + q, segment 2 st + hf
+  int koff[QS];                    // S^T operand: row q, segment 2 st + hf (key block 0)
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int st = 0; st < QS; ++st) koff[kb][st] = tile_off<HD>(32 * kb + q, 16 * st + 8 * hf);
-  int voff[OB][4][2];              // V^T operand: rows K0 + (lane%16)/4, K0 = 16 ks + 4 hf (+8)
-  {
+  for (int st = 0; st < QS; ++st) koff[st] = tile_off<HD>(q, 16 * st + 8 * hf);
+  int voff[OB][2];                 // V^T operand, k-step 0: rows 4 hf + (lane%16)/4 (+8);
+  {                                // k-step ks lies 16 ks rows further
     const int sl = lane & 15, g16 = (lane >> 4) & 1;
 #pragma unroll
     for (int j = 0; j < OB; ++j)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int row = 16 * ks + 8 * half + 4 * hf + (sl >> 2);
-          const int col = 32 * j + 16 * g16 + 4 * (sl & 3);
-          voff[j][ks][half] = tile_off<HD>(row, col);
-        }
+      for (int half = 0; half < 2; ++half)
+        voff[j][half] = tile_off<HD>(8 * half + 4 * hf + (sl >> 2), 32 * j + 16 * g16 + 4 * (sl & 3));
   }
 
   TileCopy<HD> tc;
@@ -282,7 +316,6 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   else __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  const f32x16 zero16 = {};
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t % NBUF;
     if (t + kAhead < ntiles) issue(t + kAhead);
@@ -301,60 +334,26 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
     if (!skip) {
       const __bf16* sk = sm.k[buf];
       const __bf16* sv = sm.v[buf];
-      // S^T = K Q^T. The mask enters as the initial accumulator: 0 for a visible key, -inf for
-      // a hidden one (accumulator row v of block kb is key base + 4 hf + C(kb, v),
-      // C = 32 kb + 8 (v / 4) + v % 4); full tiles start from the zero accumulator.
+      const int kbase = base + 4 * hf;
+      const int lo = g.w - kbase;
+      const int hi = bnd ? c0 + g.E - 1 - kbase : ic - kbase;
       f32x16 sacc[2];
-      if (full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          bf16x8 ka[QS];
-#pragma unroll
-          for (int st = 0; st < QS; ++st) ka[st] = *reinterpret_cast<const bf16x8*>(sk + koff[kb][st]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], zero16, 0, 0, 0);
-#pragma unroll
-          for (int st = 1; st < QS; ++st)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], sacc[kb], 0, 0, 0);
-        }
-      } else {
-        const int kbase = base + 4 * hf;
-        // visible iff lo <= C <= hi (boundary tiles: C <= hi, below c0 + E; band tiles: w .. i)
-        const int lo = g.w - kbase;
-        const int hi = bnd ? c0 + g.E - 1 - kbase : ic - kbase;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          bf16x8 ka[QS];
-#pragma unroll
-          for (int st = 0; st < QS; ++st) ka[st] = *reinterpret_cast<const bf16x8*>(sk + koff[kb][st]);
-          if (bnd) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
-              sacc[kb][v] = C <= hi ? 0.f : -INFINITY;
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
-              sacc[kb][v] = (C >= lo && C <= hi) ? 0.f : -INFINITY;
-            }
-          }
-#pragma unroll
-          for (int st = 0; st < QS; ++st)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], sacc[kb], 0, 0, 0);
-        }
-      }
+      tile_scores<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi);
       // Softmax with a lazy reference. The exact maximum is taken only while some row of the
       // wave has no reference yet, or when the tile's sum of p exceeds 2^64 (a row's scores grew
-      // far past its reference); otherwise p = 2^(s c - mc) is used as is: l and O^T share mc,
-      // so the result is exact, and p <= 2^64 keeps every value finite. Values of p far below
-      // 1 stay normal floats (bf16 and float32 share the exponent range).
+      // far past its reference; the scores are then computed again from the tile still in LDS,
+      // so they need not stay in registers); otherwise p = 2^(s c - mc) is used as is: l and
+      // O^T share mc, so the result is exact, and p <= 2^64 keeps every value finite. Values of
+      // p far below 1 stay normal floats (bf16 and float32 share the exponent range).
       bf16x8 pk[4];
       float lt = 0.f;
       bool exact = __any(mc == -INFINITY);
       if (!exact) {
         lt = tile_exp(sacc, c, mc, pk);
-        exact = __any(!(lt <= 0x1p64f));
+        if (__any(!(lt <= 0x1p64f))) {
+          exact = true;
+          tile_scores<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi);
+        }
       }
       if (exact) {
         float m4[4];
@@ -382,8 +381,8 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int j = 0; j < OB; ++j) {
-          const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][0]));
-          const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][ks][1]));
+          const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][0] + 16 * HD * ks));
+          const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, sv + voff[j][1] + 16 * HD * ks));
           const i16x4 both[2] = {vlo, vhi};
           o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(both),
                                                          pk[ks], o[j], 0, 0, 0);

@@ -121,6 +121,15 @@ SMALL_CASES = [
     ("bf16_hd128", PREFILL_BF16, dict(B=1, n=260, d=256, H=2, hd=128), None, False),
     ("bf16_hd32_N32", PREFILL_BF16, dict(B=1, n=150, d=128, H=4, hd=32, N=32, mode="train", L=5), None, False),
     ("fp32_hd64_train", TINY_FP32, dict(d=128, H=2, hd=64, n=190, P=3, L=7, layer_idx=1), None, False),
+    # every token its own chunk: each key is a boundary state, E_i = i
+    ("bf16_P1_test_L0", PREFILL_BF16, dict(B=1, n=300, d=128, H=2, P=1, L=0), None, False),
+    # chunks longer than a key tile: token-loop scan; M_train band reaching 127 tokens back
+    ("bf16_P128_train_L16", TRAIN_BF16, dict(B=1, n=700, d=128, H=2, P=128, L=16, layer_idx=5), None, False),
+    ("bf16_P64_test_L3", PREFILL_BF16, dict(B=2, n=270, d=128, H=2, P=64, L=3, layer_idx=1), None, False),
+    # hd 128 on the matrix cores with a window wider than two key tiles
+    ("bf16_hd128_train_L200", TRAIN_BF16, dict(B=1, n=520, d=256, H=2, hd=128, P=8, L=200), None, False),
+    # many short sequences: query tiles mostly past their sequence's end
+    ("bf16_tiny_seqs", PREFILL_BF16, dict(d=128, H=2, L=2, P=3, layer_idx=1), [1, 2, 3, 1, 64, 129, 0, 5], False),
 ]
 
 
@@ -244,6 +253,7 @@ def test_full_size_sampled(cfg):
     (2, 64, 16, 4, 0, 0, 12, 10, "bf16"),
     (2, 32, 16, 2, 600, 1, 300, 8, "bf16"),
     (2, 32, 16, 4, 6, 3, 17, 9, "fp32"),
+    (2, 64, 16, 1, 1, 0, 5, 7, "bf16"),       # every position ends a chunk; window of one
 ])
 def test_decode_matches_prefill_rows(H, hd, N, P, L, layer, n0, steps, dtype):
     say(f"decode H={H} hd={hd} N={N} P={P} L={L} layer={layer} n0={n0} dtype={dtype}")
@@ -311,3 +321,71 @@ def test_decode_rejects_full_cache_and_bad_mirror():
     with pytest.raises(att.AttambaError) as e:
         att.decode_step(cache, *args)
     assert e.value.status == 2
+
+
+def test_decode_snapshot_resume_bit_exact():
+    """The cache buffers plus the host mirrors (pos, n_bound) are the whole decode state: a
+    snapshot restored after more steps replays those steps with identical outputs."""
+    B, H, hd, N, P, L, layer = 2, 4, 64, 16, 4, 6, 1
+    d = H * hd
+    cfg = PREFILL_BF16.with_(B=B, n=64, d=d, H=H, hd=hd, N=N, P=P, L=L, layer_idx=layer)
+    inp = make_prefill(cfg, seed=77)
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    cache = att.DecodeCache(B, H, hd, N, P, L, layer, 64 // P + 4, torch.bfloat16, inp.param,
+                            pos=0, n_bound=0)
+
+    def step(i):
+        rows = torch.from_numpy(inp.seq_cu[:-1] + i).long().cuda()
+        return att.decode_step(cache, act["q"][rows].view(B, H, hd).contiguous(),
+                               act["x"][rows].contiguous(), act["dt_k"][rows].contiguous(),
+                               act["dt_v"][rows].contiguous(), act["bm_k"][rows].contiguous(),
+                               act["cm_k"][rows].contiguous(), act["bm_v"][rows].contiguous(),
+                               act["cm_v"][rows].contiguous()).clone()
+
+    for i in range(13):
+        step(i)
+    names = ("kb", "vb", "kw", "vw", "h_k", "h_v")
+    snap = {k: getattr(cache, k).clone() for k in names}
+    pos, nb = cache.pos, cache.n_bound
+    first = [step(i) for i in range(13, 30)]
+    for k in names:
+        getattr(cache, k).copy_(snap[k])
+    cache.set_position(pos, nb)
+    second = [step(i) for i in range(13, 30)]
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)
+    assert cache.pos == 30
+
+
+@pytest.mark.parametrize("hd,mode,L", [(64, "test", 64), (128, "train", 5), (64, "test", 0)])
+def test_attention_growing_scores(hd, mode, L):
+    """Scores that grow along the sequence by far more than 2^64 per row (keys k_j = a_j u with
+    a_j rising, queries along u) force the rare exact-maximum path of the lazy softmax again
+    and again, and scores that fall far below the first ones must not disturb the result."""
+    say(f"attention growing scores hd={hd} mode={mode} L={L}")
+    rng = np.random.default_rng(hd + L)
+    n, H, P = 700, 2, 4
+    seq_cu = np.array([0, n], dtype=np.int32)
+    u = rng.standard_normal(hd)
+    u /= np.linalg.norm(u)
+    a = np.concatenate([np.linspace(0.0, 60.0, n // 2), np.linspace(60.0, -40.0, n - n // 2)])
+    k = (a[:, None, None] * u[None, None, :] + 0.05 * rng.standard_normal((n, H, hd)))
+    q = np.sqrt(hd) * np.ones((n, H, 1)) * u[None, None, :] + 0.05 * rng.standard_normal((n, H, hd))
+    v = rng.standard_normal((n, H, hd))
+    bf = lambda x: torch.from_numpy(x).to(torch.bfloat16)
+    qt, kt, vt = bf(q), bf(k), bf(v)
+    cu, tc, ie = oracle.segment(seq_cu, P, 0)
+    ends = np.asarray(cu[1:], dtype=np.int64) - 1
+    dev = lambda t: t.contiguous().cuda()
+    out, lse = att.chunk_attn_fwd(dev(qt), dev(kt), dev(vt), dev(kt[ends]), dev(vt[ends]),
+                                  torch.from_numpy(seq_cu).cuda(), torch.from_numpy(np.asarray(cu, dtype=np.int32)).cuda(),
+                                  torch.from_numpy(tc.astype(np.int32)).cuda(), n, L, MODE[mode])
+    torch.cuda.synchronize()
+    f = lambda t: t.double().numpy()
+    ref_o, ref_l = oracle.chunk_attention(f(qt), f(kt), f(vt), seq_cu, tc, ie, L, mode)
+    check_close(out.float().cpu().numpy(), ref_o, "bf16", "out")
+    got_l = lse.cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert (np.isfinite(got_l) == fin).all()
+    check_close(got_l[fin], ref_l[fin], "bf16", "lse")
