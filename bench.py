@@ -7,6 +7,7 @@ N=16, P=8, L=64, uniform chunks, M_test + window). Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload prefill_bf16|varchunk_bf16|train_bf16]
     python bench.py --workload decode_bf16      # decode configuration, separate line
+    python bench.py --workload proj_bf16        # input projections (x W^T) at the prefill shape
     python bench.py --workload copy             # reference bandwidth (512 MiB device copy)
 """
 from __future__ import annotations
@@ -321,6 +322,52 @@ def bench_decode(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_proj(args):
+    """The layer's input projections at the prefill shape: Y = x W^T with x [16384, 2048] and
+    the stacked weight W [3 d + 4 N, d] (q, dt_K, dt_V, Bm_K, Cm_K, Bm_V, Cm_V), bf16."""
+    import torch
+    import ssm_compressed_chunked_amd as att
+    from workloads import PREFILL_CONFIGS, make_projection
+    cfg = PREFILL_CONFIGS["prefill_bf16"]
+    T, d, N = cfg.T, cfg.d, cfg.N
+    inp = make_projection(T, d, N, seed=cfg.seed)
+    x, w = inp.x.cuda(), inp.w.cuda()
+    outs = [torch.empty((T, wd), dtype=torch.bfloat16, device="cuda") for wd in inp.widths]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        att.input_proj(x, w, inp.widths, outs=outs, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        att.input_proj(x, w, inp.widths, outs=outs, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        att.input_proj(x, w, inp.widths, outs=outs, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    n_out = sum(inp.widths)
+    flop = 2.0 * T * d * n_out
+    tflops = flop / (us * 1e-6) / 1e12
+    traffic = measured_traffic("proj_gemm_kernel", ["proj_gemm.hip", "common.h"])
+    print(json.dumps({
+        "metric": "input projections TFLOP/s (x W^T, bf16)", "value": round(tflops, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "proj_bf16", "T": T, "d": d, "n_out": n_out,
+                   "segments": inp.widths},
+        "roofline": {"bound": "mfma", "kernel": "proj_gemm_kernel", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "avg_launch_us": round(us, 2)}}), flush=True)
+
+
 def bench_copy(args):
     """A plain device copy of 512 MiB: the reference point that scales rocprofv3's FETCH_SIZE
     and WRITE_SIZE counters to bytes (the copy moves exactly 512 MiB each way per launch)."""
@@ -361,6 +408,8 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     if args.workload == "copy":
         bench_copy(args)
+    elif args.workload == "proj_bf16":
+        bench_proj(args)
     elif args.workload.startswith("decode"):
         bench_decode(args)
     else:

@@ -245,6 +245,37 @@ int attamba_decode_workspace_size(const attamba_decode_cache* cache, size_t* byt
 int attamba_decode_step(attamba_decode_cache* cache, const attamba_decode_inputs* in,
                         attamba_stream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Input projections (the step just before the path: the queries and the per-token inputs
+ * dt, Bm, Cm of SSM_K and SSM_V are linear maps of the layer input; pith.science "Core claim":
+ * the SSMs replace the key and value projections; the selective SSM's inputs are the paper's
+ * Eq. 3, cited in "Assumptions & free parameters").
+ *
+ * Y = x W^T, bf16 inputs, fp32 accumulation, bf16 outputs:
+ *   x    [T, d]      row-major, the layer input;
+ *   w    [n_out, d]  row-major, one row per output feature (the stacked weights, e.g. q, dt_K,
+ *                    dt_V, Bm_K, Cm_K, Bm_V, Cm_V: n_out = 3 d + 4 N);
+ *   the n_out features form n_seg consecutive segments: segment i holds features
+ *   seg_start[i] .. seg_start[i+1]-1 and is written to out[i] as a row-major
+ *   [T, seg_start[i+1] - seg_start[i]] tensor.
+ * All pointers are device pointers owned by the caller; nothing is allocated.
+ * Errors: NULL_ARG (x, w or a used out[i]); BAD_SHAPE (T < 0, d < 64 or not a multiple of 64,
+ * n_out < 1, n_seg outside 1..ATTAMBA_PROJ_MAX_SEGMENTS, seg_start not starting at 0, not
+ * increasing, not ending at n_out, or a segment start not a multiple of 4); UNSUPPORTED (dtype
+ * other than bf16, or T*d, n_out*d or T*n_out at or above 2^31); HIP.
+ * ---------------------------------------------------------------------------------------- */
+#define ATTAMBA_PROJ_MAX_SEGMENTS 8
+typedef struct {
+  int32_t T, d, n_out, dtype;              /* dtype: ATTAMBA_BF16 */
+  int32_t n_seg;
+  const void* x;
+  const void* w;
+  int32_t seg_start[ATTAMBA_PROJ_MAX_SEGMENTS + 1];
+  void* out[ATTAMBA_PROJ_MAX_SEGMENTS];
+} attamba_proj_args;
+
+int attamba_input_proj(const attamba_proj_args* args, attamba_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

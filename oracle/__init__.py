@@ -5,6 +5,6 @@ baseline; never by the product path.
 """
 from .attamba_oracle import (TEST, TRAIN, DecodeSeq, boundary_states, chunk_attention,
                              decode_state_from_prefix, decode_step, dense_mask,
-                             is_chunk_end_at, is_chunk_start_at, kvssm_forward,
+                             is_chunk_end_at, is_chunk_start_at, kvssm_forward, linear,
                              masked_attention, segment, selective_scan, softplus,
                              uniform_chunk_starts)

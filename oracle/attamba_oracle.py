@@ -37,6 +37,19 @@ TRAIN, TEST = "train", "test"
 
 
 # ----------------------------------------------------------------------------------------
+# Input projections: queries and the SSMs' per-token inputs dt, Bm, Cm are linear maps of the
+# layer input (pith.science "Core claim": the SSMs replace the key and value projections; the
+# selective SSM's inputs, the paper's Eq. 3, cited in "Assumptions & free parameters").
+# ----------------------------------------------------------------------------------------
+def linear(x, w):
+    """y[t, f] = sum_k x[t, k] * w[f, k]: x [T, d], w [n_out, d] (one row per output
+    feature). Returns float64 [T, n_out]."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    return x @ w.T
+
+
+# ----------------------------------------------------------------------------------------
 # Segmentation: uniform chunks of P tokens with a cyclic offset per layer (pith.science
 # "What carries the argument": cyclic chunking shifts the chunk offset by layer index;
 # "Assumptions & free parameters": offset = layer index), or variable-length chunks given

@@ -35,6 +35,15 @@ class ScanArgs(C.Structure):
                 ("h_last_k", _vp), ("h_last_v", _vp)]
 
 
+PROJ_MAX_SEGMENTS = 8
+
+
+class ProjArgs(C.Structure):
+    _fields_ = [("T", _i32), ("d", _i32), ("n_out", _i32), ("dtype", _i32), ("n_seg", _i32),
+                ("x", _vp), ("w", _vp), ("seg_start", _i32 * (PROJ_MAX_SEGMENTS + 1)),
+                ("out", _vp * PROJ_MAX_SEGMENTS)]
+
+
 class AttnArgs(C.Structure):
     _fields_ = [("T", _i32), ("H", _i32), ("hd", _i32), ("dtype", _i32), ("S", _i32),
                 ("max_seqlen", _i32), ("n_chunks", _i32), ("L", _i32), ("mode", _i32),
@@ -67,6 +76,7 @@ EXPORTS = {
     "attamba_chunk_index": ([_vp, _i32, _i32, _vp, _vp, _vp], C.c_int),
     "attamba_kvssm_scan": ([C.POINTER(ScanArgs), _vp], C.c_int),
     "attamba_chunk_attn_fwd": ([C.POINTER(AttnArgs), _vp], C.c_int),
+    "attamba_input_proj": ([C.POINTER(ProjArgs), _vp], C.c_int),
     "attamba_decode_workspace_size": ([C.POINTER(DecodeCacheStruct), C.POINTER(C.c_size_t)],
                                       C.c_int),
     "attamba_decode_step": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodeInputsStruct), _vp],
@@ -228,6 +238,32 @@ def kvssm_scan(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k
     a.h_last_v = _dev(hv, "h_last_v")
     _check(lib().attamba_kvssm_scan(C.byref(a), _stream(stream)))
     return dict(y_k=y_k, y_v=y_v, kb=kb, vb=vb, h_last_k=hk, h_last_v=hv)
+
+
+def input_proj(x: torch.Tensor, w: torch.Tensor, widths, outs=None, stream=None):
+    """Y = x w^T (bf16, fp32 accumulation) split by features into len(widths) row-major
+    tensors [T, widths[i]]: x [T, d], w [sum(widths), d]. Returns the list of outputs."""
+    T, d = x.shape
+    n_out = int(sum(widths))
+    if w.shape != (n_out, d):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected {(n_out, d)}")
+    if not 1 <= len(widths) <= PROJ_MAX_SEGMENTS:
+        raise ValueError(f"1 .. {PROJ_MAX_SEGMENTS} output segments")
+    if outs is None:
+        outs = [torch.empty((T, int(wd)), dtype=x.dtype, device=x.device) for wd in widths]
+    a = ProjArgs()
+    a.T, a.d, a.n_out, a.n_seg = T, d, n_out, len(widths)
+    a.dtype = _dtype_code(x)
+    a.x = _dev(x, "x", torch.bfloat16, T * d)
+    a.w = _dev(w, "w", torch.bfloat16, n_out * d)
+    start = 0
+    for i, wd in enumerate(widths):
+        a.seg_start[i] = start
+        a.out[i] = _dev(outs[i], f"out[{i}]", torch.bfloat16, T * int(wd))
+        start += int(wd)
+    a.seg_start[len(widths)] = start
+    _check(lib().attamba_input_proj(C.byref(a), _stream(stream)))
+    return outs
 
 
 def chunk_attn_fwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: int, L: int,

@@ -184,6 +184,34 @@ int attamba_chunk_attn_fwd(const attamba_attn_args* a, attamba_stream_t stream) 
                     "chunk_attn_fwd launch");
 }
 
+int attamba_input_proj(const attamba_proj_args* a, attamba_stream_t stream) {
+  if (!a) return fail(ATTAMBA_ERR_NULL_ARG, "input_proj: args null");
+  if (!dtype_ok(a->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "input_proj: dtype %d", a->dtype);
+  if (a->dtype != ATTAMBA_BF16) return fail(ATTAMBA_ERR_UNSUPPORTED, "input_proj: only bf16 is built");
+  if (a->T < 0 || a->d < 64 || a->d % 64 != 0 || a->n_out < 1 || a->n_seg < 1 ||
+      a->n_seg > ATTAMBA_PROJ_MAX_SEGMENTS)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "input_proj: T=%d d=%d n_out=%d n_seg=%d", a->T, a->d, a->n_out, a->n_seg);
+  if (a->seg_start[0] != 0 || a->seg_start[a->n_seg] != a->n_out)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "input_proj: segments must cover features 0 .. n_out");
+  for (int i = 0; i < a->n_seg; ++i)
+    if (a->seg_start[i + 1] <= a->seg_start[i] || a->seg_start[i] % 4 != 0)
+      return fail(ATTAMBA_ERR_BAD_SHAPE, "input_proj: segment %d (start %d, end %d) empty or start not a multiple of 4",
+                  i, a->seg_start[i], a->seg_start[i + 1]);
+  if (static_cast<int64_t>(a->T) * a->d > INT32_MAX || static_cast<int64_t>(a->n_out) * a->d > INT32_MAX ||
+      static_cast<int64_t>(a->T) * a->n_out > INT32_MAX)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "input_proj: T*d, n_out*d or T*n_out exceeds 2^31 elements");
+  if (!a->x || !a->w) return fail(ATTAMBA_ERR_NULL_ARG, "input_proj: x or w null");
+  for (int i = 0; i < a->n_seg; ++i)
+    if (!a->out[i]) return fail(ATTAMBA_ERR_NULL_ARG, "input_proj: out[%d] null", i);
+  attamba::ProjParams p{};
+  p.T = a->T; p.d = a->d; p.n_out = a->n_out; p.n_seg = a->n_seg;
+  p.x = a->x; p.w = a->w;
+  for (int i = 0; i <= ATTAMBA_PROJ_MAX_SEGMENTS; ++i)
+    p.seg_start[i] = i <= a->n_seg ? a->seg_start[i] : a->n_out;
+  for (int i = 0; i < ATTAMBA_PROJ_MAX_SEGMENTS; ++i) p.out[i] = i < a->n_seg ? a->out[i] : nullptr;
+  return hip_status(attamba::launch_proj_gemm(p, reinterpret_cast<hipStream_t>(stream)), "input_proj launch");
+}
+
 int attamba_decode_workspace_size(const attamba_decode_cache* c, size_t* bytes) {
   if (!c || !bytes) return fail(ATTAMBA_ERR_NULL_ARG, "decode_workspace_size: null pointer");
   if (c->B < 1 || c->H < 1 || c->hd < 1 || c->cap < 0 || c->L < 0)

@@ -38,6 +38,17 @@ struct DecodeLaunch {
   int n_splits;
   float scale;
 };
+// Input projection GEMM (bf16): Y = x W^T split into feature segments.
+constexpr int kMaxProjSegments = ATTAMBA_PROJ_MAX_SEGMENTS;
+struct ProjParams {
+  int T, d, n_out, n_seg;
+  const void* x;
+  const void* w;
+  int seg_start[kMaxProjSegments + 1];
+  void* out[kMaxProjSegments];
+};
+hipError_t launch_proj_gemm(const ProjParams& p, hipStream_t stream);
+
 int decode_max_splits(int cap, int L);
 size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L);
 hipError_t launch_decode_step(const attamba_decode_cache& c, const attamba_decode_inputs& in,

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_and_exports_agree():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(B.EXPORTS), (set(names) ^ set(B.EXPORTS))
     lib = att.lib()
     for n in names:
@@ -100,3 +100,30 @@ def test_device_entry_points_validate_before_launch():
     assert lib.attamba_decode_step(C.byref(c), C.byref(i), None) == B.ERR_BAD_SHAPE
     c.d, c.hd, c.H = 96, 48, 2
     assert lib.attamba_decode_step(C.byref(c), C.byref(i), None) == B.ERR_UNSUPPORTED
+
+
+def test_input_proj_validates_before_launch():
+    lib = att.lib()
+    assert lib.attamba_input_proj(None, None) == B.ERR_NULL_ARG
+    a = B.ProjArgs()
+    a.T, a.d, a.n_out, a.dtype, a.n_seg = 16, 128, 24, 5, 2
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_DTYPE
+    a.dtype = B.FP32
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_UNSUPPORTED
+    a.dtype = B.BF16
+    a.seg_start[0], a.seg_start[1], a.seg_start[2] = 0, 16, 24
+    a.d = 96
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # d not a multiple of 64
+    a.d = 128
+    a.seg_start[1] = 18
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # start not 4-aligned
+    a.seg_start[1] = 16
+    a.seg_start[2] = 20
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # does not reach n_out
+    a.seg_start[2] = 24
+    a.n_seg = 9
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # too many segments
+    a.n_seg = 2
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_NULL_ARG       # x, w, out null
+    a.T = 1 << 24
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_UNSUPPORTED    # T*d >= 2^31

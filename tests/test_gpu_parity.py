@@ -14,7 +14,7 @@ import torch
 import oracle
 import ssm_compressed_chunked_amd as att
 from ssm_compressed_chunked_amd.pipeline import chunk_layout, prefill_forward
-from workloads import (PREFILL_BF16, TINY_FP32, TRAIN_BF16, VARCHUNK_BF16, make_prefill,
+from workloads import (PREFILL_BF16, TINY_FP32, TRAIN_BF16, VARCHUNK_BF16, make_prefill, make_projection,
                        make_ragged_prefill)
 
 pytestmark = pytest.mark.gpu
@@ -389,3 +389,41 @@ def test_attention_growing_scores(hd, mode, L):
     fin = np.isfinite(ref_l)
     assert (np.isfinite(got_l) == fin).all()
     check_close(got_l[fin], ref_l[fin], "bf16", "lse")
+
+
+# ------------------------------------------------------------------------ input projections
+@pytest.mark.parametrize("T,d,widths", [
+    (300, 128, [128, 128, 128, 16, 16, 16, 16]),   # the layer's seven outputs, ragged token tail
+    (129, 64, [64, 4, 60]),                         # feature segments inside one tile
+    (1, 256, [256]),
+    (517, 192, [192, 192, 192, 32, 32, 32, 32, 4]),  # N = 32, eight segments, ragged both ways
+])
+def test_input_proj_elementwise(T, d, widths):
+    say(f"input_proj T={T} d={d} widths={widths}")
+    n_out = sum(widths)
+    inp = make_projection(T, d, 16, seed=T + d)
+    rng = np.random.default_rng(T)
+    w = (torch.from_numpy(rng.standard_normal((n_out, d)).astype(np.float32)) * 0.02).to(torch.bfloat16)
+    outs = att.input_proj(inp.x.cuda(), w.cuda(), widths)
+    torch.cuda.synchronize()
+    ref = oracle.linear(inp.x.double().numpy(), w.double().numpy())
+    start = 0
+    for i, wd in enumerate(widths):
+        check_close(outs[i].float().cpu().numpy(), ref[:, start:start + wd], "bf16", f"segment {i}")
+        start += wd
+
+
+def test_input_proj_full_size_sampled():
+    """The projection of the prefill workload (T = 16384, d = 2048, N = 16) in the launch
+    configuration the benchmark times, checked on sampled rows (tile edges included)."""
+    T, d, N = 16384, 2048, 16
+    inp = make_projection(T, d, N, seed=2)
+    outs = att.input_proj(inp.x.cuda(), inp.w.cuda(), inp.widths)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 129, 4095, 8191, 8192, 12000, T - 129, T - 2, T - 1])
+    ref = oracle.linear(inp.x[rows].double().numpy(), inp.w.double().numpy())
+    start = 0
+    for i, wd in enumerate(inp.widths):
+        got = outs[i][torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        check_close(got, ref[:, start:start + wd], "bf16", f"segment {i}")
+        start += wd

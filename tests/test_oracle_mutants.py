@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "attamba_oracle.py")
 PINS = ["test_oracle_segment.py", "test_oracle_scan.py", "test_oracle_attention.py",
-        "test_oracle_decode.py"]
+        "test_oracle_decode.py", "test_oracle_proj.py"]
 
 MUTANTS = [
     ("decay uses the previous step size", "decay = np.exp(delta[k][:, None] * A)",
@@ -46,6 +46,9 @@ MUTANTS = [
     ("LSE without the max", "lse[h, live] = mx[live] + np.log(denom[live])",
      "lse[h, live] = np.log(denom[live])"),
     ("chunk end flag at chunk start", "is_end[chunk_cu[q + 1] - 1] = 1", "is_end[chunk_cu[q]] = 1"),
+    ("projection weight not transposed", "return x @ w.T", "return x @ w"),
+    ("projection output features reversed", "return x @ w.T", "return (x @ w.T)[:, ::-1]"),
+    ("projection with a dropped input feature", "return x @ w.T", "return x[:, 1:] @ w[:, 1:].T"),
     ("first chunk not shortened by the offset", "return [t for t in range(n) if t == 0 or (t - o) % P == 0]",
      "return [t for t in range(n) if t % P == 0]"),
 ]

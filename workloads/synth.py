@@ -117,6 +117,26 @@ def make_ragged_prefill(base: PrefillConfig, lengths: list[int], seed: int,
 
 
 @dataclass
+class ProjInputs:
+    """Layer input x [T, d] and the stacked projection weight w [n_out, d] (one row per
+    output feature: q, dt_K, dt_V rows of width d, then Bm_K, Cm_K, Bm_V, Cm_V of width N),
+    both in bf16 (CPU tensors), and the segment widths in that order."""
+    x: torch.Tensor
+    w: torch.Tensor
+    widths: list
+
+
+def make_projection(T: int, d: int, N: int, seed: int) -> ProjInputs:
+    """x ~ N(0, 1) and every weight ~ N(0, 0.02^2), as for the prefill inputs."""
+    rng = np.random.default_rng((seed, 2))
+    widths = [d, d, d, N, N, N, N]
+    x = rng.standard_normal((T, d), dtype=np.float32)
+    w = rng.standard_normal((sum(widths), d), dtype=np.float32) * np.float32(0.02)
+    return ProjInputs(x=torch.from_numpy(x).to(torch.bfloat16),
+                      w=torch.from_numpy(w).to(torch.bfloat16), widths=widths)
+
+
+@dataclass
 class DecodeInputs:
     """Synthetic decode workload: a cache of `n_bound` boundary states and an L-slot window
     per sequence (N(0,1) values rounded to the storage type), zero SSM state, and per-step
