@@ -8,6 +8,7 @@ N=16, P=8, L=64, uniform chunks, M_test + window). Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload prefill_bf16|varchunk_bf16|train_bf16]
     python bench.py --workload decode_bf16      # decode configuration, separate line
     python bench.py --workload proj_bf16        # input projections (x W^T) at the prefill shape
+    python bench.py --workload layer_bf16       # projections + KV-SSM forward from the layer input
     python bench.py --workload copy             # reference bandwidth (512 MiB device copy)
 """
 from __future__ import annotations
@@ -368,6 +369,61 @@ def bench_proj(args):
                      "avg_launch_us": round(us, 2)}}), flush=True)
 
 
+def bench_layer(args):
+    """One layer from its input x at the prefill shape: the input projections (x W^T on the
+    matrix cores) followed by the KV-SSM forward (segmentation, scan, attention)."""
+    import torch
+    import ssm_compressed_chunked_amd as att
+    from workloads import PREFILL_CONFIGS, make_prefill, make_projection
+    cfg = PREFILL_CONFIGS["prefill_bf16"]
+    T, d, H, hd, N = cfg.T, cfg.d, cfg.H, cfg.hd, cfg.N
+    pj = make_projection(T, d, N, seed=cfg.seed)
+    par = {k: v.cuda() for k, v in make_prefill(cfg.with_(B=1, n=256)).param.items()}
+    x, w = pj.x.cuda(), pj.w.cuda()
+    seq_cu_h = (np.arange(cfg.B + 1) * cfg.n).astype(np.int32)
+    seq_cu = torch.from_numpy(seq_cu_h).cuda()
+    n = att.count_chunks(seq_cu_h, cfg.P, cfg.layer_idx)
+    widths = pj.widths
+    proj = [torch.empty((T, wd), dtype=torch.bfloat16, device="cuda") for wd in widths]
+    q, dtk, dtv, bmk, cmk, bmv, cmv = proj
+    chunk_cu = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    token_chunk = torch.empty(T, dtype=torch.int32, device="cuda")
+    is_end = torch.empty(T, dtype=torch.uint8, device="cuda")
+    y_k, y_v = torch.empty_like(x), torch.empty_like(x)
+    kb = torch.empty((n, d), dtype=x.dtype, device="cuda")
+    vb = torch.empty_like(kb)
+    out = torch.empty((T, H, hd), dtype=x.dtype, device="cuda")
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        att.input_proj(x, w, widths, outs=proj, stream=stream)
+        att.chunk_boundaries(seq_cu, T, cfg.P, cfg.layer_idx, n, chunk_cu, token_chunk, is_end,
+                             stream=stream)
+        att.kvssm_scan(x, dtk, dtv, bmk, cmk, bmv, cmv, par["A_k"], par["A_v"], par["D_k"],
+                       par["D_v"], par["bias_k"], par["bias_v"], chunk_cu, y_k=y_k, y_v=y_v,
+                       kb=kb, vb=vb, stream=stream)
+        att.chunk_attn_fwd(q.view(T, H, hd), y_k.view(T, H, hd), y_v.view(T, H, hd),
+                           kb.view(n, H, hd), vb.view(n, H, hd), seq_cu, chunk_cu, token_chunk,
+                           cfg.n, cfg.L, att.MASK_TEST, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(json.dumps({
+        "metric": "tokens/sec, input projections + KV-SSM forward", "value": round(T * args.steps / wall, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "layer_bf16", "B": cfg.B, "n": cfg.n, "d_model": d, "heads": H,
+                   "head_dim": hd, "N": N, "P": cfg.P, "L": cfg.L}}), flush=True)
+
+
 def bench_copy(args):
     """A plain device copy of 512 MiB: the reference point that scales rocprofv3's FETCH_SIZE
     and WRITE_SIZE counters to bytes (the copy moves exactly 512 MiB each way per launch)."""
@@ -410,6 +466,8 @@ def main():
         bench_copy(args)
     elif args.workload == "proj_bf16":
         bench_proj(args)
+    elif args.workload == "layer_bf16":
+        bench_layer(args)
     elif args.workload.startswith("decode"):
         bench_decode(args)
     else:

@@ -1,5 +1,6 @@
-"""The prefill forward as the three library calls in order (marshalling only):
-segmentation -> KV-SSM scan -> chunk attention, all enqueued on the current stream."""
+"""The prefill forward as the library calls in order (marshalling only):
+[input projections ->] segmentation -> KV-SSM scan -> chunk attention, all enqueued on the
+current stream."""
 from __future__ import annotations
 
 from dataclasses import dataclass
@@ -58,3 +59,23 @@ def prefill_forward(act: dict, params: dict, seq_cu_host, H: int, hd: int, P: in
                                 layout.token_chunk, max(max_len, 1), L, mode,
                                 return_lse=want_lse, stream=stream)
     return dict(layout=layout, scan=scan, out=out, lse=lse, seq_cu=seq_cu)
+
+
+PROJ_NAMES = ("q", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v")
+
+
+def layer_forward(x: torch.Tensor, w_stack: torch.Tensor, params: dict, seq_cu_host, H: int,
+                  hd: int, N: int, P: int | None, layer_idx: int, L: int, mode: int,
+                  chunk_lens=None, stream=None, want_lse: bool = True) -> dict:
+    """One layer from its input: x [T, d] (bf16) and the stacked projection weight w_stack
+    [3 d + 4 N, d] (rows: q, dt_K, dt_V, Bm_K, Cm_K, Bm_V, Cm_V) -> the input projections on the
+    matrix cores, then the KV-SSM forward of `prefill_forward`. The layer index sets the cyclic
+    chunk offset, so consecutive layers of a model use shifted chunk boundaries."""
+    T, d = x.shape
+    outs = B.input_proj(x, w_stack, [d, d, d, N, N, N, N], stream=stream)
+    act = dict(zip(PROJ_NAMES, outs))
+    act["x"] = x
+    res = prefill_forward(act, params, seq_cu_host, H, hd, P, layer_idx, L, mode,
+                          chunk_lens=chunk_lens, stream=stream, want_lse=want_lse)
+    res["proj"] = act
+    return res

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import ssm_compressed_chunked_amd as att
-from ssm_compressed_chunked_amd.pipeline import chunk_layout, prefill_forward
+from ssm_compressed_chunked_amd.pipeline import chunk_layout, layer_forward, prefill_forward
 from workloads import (PREFILL_BF16, TINY_FP32, TRAIN_BF16, VARCHUNK_BF16, make_prefill, make_projection,
                        make_ragged_prefill)
 
@@ -427,3 +427,31 @@ def test_input_proj_full_size_sampled():
         got = outs[i][torch.from_numpy(rows).cuda()].float().cpu().numpy()
         check_close(got, ref[:, start:start + wd], "bf16", f"segment {i}")
         start += wd
+
+
+@pytest.mark.parametrize("layer", [0, 3, 6])
+def test_layer_forward_from_x(layer):
+    """Projections on the matrix cores feeding the KV-SSM forward, for three layers whose
+    chunk boundaries are shifted by the layer index. The oracle projects in float64 and rounds
+    to bf16 with round-to-nearest-even, the storage type the GPU path hands to the scan."""
+    T, d, H, hd, N, P, L = 330, 128, 2, 64, 16, 4, 5
+    say(f"layer forward layer={layer}")
+    pj = make_projection(T, d, N, seed=40 + layer)
+    par = make_prefill(PREFILL_BF16.with_(B=1, n=T, d=d, H=H, hd=hd, N=N), seed=41).param
+    seq_cu = np.array([0, 200, T], dtype=np.int32)
+    res = layer_forward(pj.x.cuda(), pj.w.cuda(), {k: v.cuda() for k, v in par.items()}, seq_cu,
+                        H, hd, N, P, layer, L, att.MASK_TEST)
+    torch.cuda.synchronize()
+    proj = oracle.linear(pj.x.double().numpy(), pj.w.double().numpy())
+    proj = torch.from_numpy(proj).to(torch.bfloat16).double().numpy()   # storage rounding
+    f = {"x": pj.x.double().numpy()}
+    start = 0
+    for name, wd in zip(("q", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v"), [d, d, d, N, N, N, N]):
+        f[name] = proj[:, start:start + wd]
+        start += wd
+    for k, v in par.items():
+        f[k] = v.double().numpy()
+    ref = oracle.kvssm_forward(f, seq_cu, H, hd, P, layer, L, "test")
+    np.testing.assert_array_equal(res["layout"].chunk_cu.cpu().numpy(), ref["chunk_cu"])
+    check_close(res["scan"]["y_k"].float().cpu().numpy(), ref["y_k"], "bf16", "y_k")
+    check_close(res["out"].float().cpu().numpy(), ref["out"], "bf16", "out")
