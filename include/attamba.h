@@ -113,6 +113,9 @@ int attamba_chunk_index(const int32_t* chunk_cu, int32_t n_chunks, int32_t T,
  *   h[c,:] = exp(delta * A_S[c,:]) * h[c,:] + delta * x[t,c] * bm_S[t,:]
  *   y_S[t,c] = sum_n cm_S[t,n] * h[c,n] + D_S[c] * x[t,c]
  * The boundary state of chunk q is the output at its last token (the review's K^(p)[-1]).
+ * Both SSMs read the layer input x. For the variant that keeps explicit key and value
+ * projections in front of the SSMs (pith.science "If this is right": dropping them costs
+ * about 1 % perplexity), x_v gives SSM_V its own input (x then feeds SSM_K only).
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t T;        /* tokens in the packed batch (>= 0) */
@@ -143,6 +146,7 @@ typedef struct {
   int32_t S;
   float* h_last_k;                    /* [S, d, N] out or NULL */
   float* h_last_v;                    /* [S, d, N] out or NULL */
+  const void* x_v;                    /* [T, d] input of SSM_V, or NULL: SSM_V reads x */
 } attamba_scan_args;
 
 /* Errors: NULL_ARG, BAD_SHAPE (T, n_chunks < 0; d not a positive multiple of 64),
@@ -264,7 +268,7 @@ int attamba_decode_step(attamba_decode_cache* cache, const attamba_decode_inputs
  * increasing, not ending at n_out, or a segment start not a multiple of 4); UNSUPPORTED (dtype
  * other than bf16, or T*d, n_out*d or T*n_out at or above 2^31); HIP.
  * ---------------------------------------------------------------------------------------- */
-#define ATTAMBA_PROJ_MAX_SEGMENTS 8
+#define ATTAMBA_PROJ_MAX_SEGMENTS 12
 typedef struct {
   int32_t T, d, n_out, dtype;              /* dtype: ATTAMBA_BF16 */
   int32_t n_seg;

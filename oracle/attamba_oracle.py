@@ -235,8 +235,10 @@ def kvssm_forward(inp: dict, seq_cu, H: int, hd: int, P: int | None, layer_idx: 
     chunk_cu, token_chunk, is_end = segment(seq_cu, P, layer_idx, chunk_lens)
     y_k, _ = selective_scan(inp["x"], inp["dt_k"], inp["bias_k"], inp["A_k"], inp["bm_k"],
                             inp["cm_k"], inp["D_k"], chunk_cu)
-    y_v, _ = selective_scan(inp["x"], inp["dt_v"], inp["bias_v"], inp["A_v"], inp["bm_v"],
-                            inp["cm_v"], inp["D_v"], chunk_cu)
+    # SSM_V reads x, or its own input x_v (explicit key and value projections kept in front of
+    # the SSMs, pith.science "If this is right")
+    y_v, _ = selective_scan(inp.get("x_v", inp["x"]), inp["dt_v"], inp["bias_v"], inp["A_v"],
+                            inp["bm_v"], inp["cm_v"], inp["D_v"], chunk_cu)
     T = y_k.shape[0]
     k3 = y_k.reshape(T, H, hd)
     v3 = y_v.reshape(T, H, hd)

@@ -32,10 +32,10 @@ class ScanArgs(C.Structure):
                 ("cm_k", _vp), ("bm_v", _vp), ("cm_v", _vp), ("A_k", _vp), ("A_v", _vp),
                 ("D_k", _vp), ("D_v", _vp), ("bias_k", _vp), ("bias_v", _vp), ("y_k", _vp),
                 ("y_v", _vp), ("kb", _vp), ("vb", _vp), ("seq_cu", _vp), ("S", _i32),
-                ("h_last_k", _vp), ("h_last_v", _vp)]
+                ("h_last_k", _vp), ("h_last_v", _vp), ("x_v", _vp)]
 
 
-PROJ_MAX_SEGMENTS = 8
+PROJ_MAX_SEGMENTS = 12
 
 
 class ProjArgs(C.Structure):
@@ -200,8 +200,9 @@ def chunk_index(chunk_cu: torch.Tensor, T: int, token_chunk=None, is_end=None, s
 
 def kvssm_scan(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k, bias_v,
                chunk_cu, *, y_k=None, y_v=None, kb=None, vb=None, boundaries=True,
-               seq_cu=None, h_last=False, stream=None) -> dict:
-    """Both selective scans in one pass. Returns dict(y_k, y_v, kb, vb, h_last_k, h_last_v)."""
+               seq_cu=None, h_last=False, x_v=None, stream=None) -> dict:
+    """Both selective scans in one pass. x_v: optional separate input of SSM_V (x then feeds
+    SSM_K only). Returns dict(y_k, y_v, kb, vb, h_last_k, h_last_v)."""
     T, d = x.shape
     N = A_k.shape[1]
     n_chunks = chunk_cu.numel() - 1
@@ -236,6 +237,7 @@ def kvssm_scan(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k
     a.S = S
     a.h_last_k = _dev(hk, "h_last_k")
     a.h_last_v = _dev(hv, "h_last_v")
+    a.x_v = _dev(x_v, "x_v", act, T * d)
     _check(lib().attamba_kvssm_scan(C.byref(a), _stream(stream)))
     return dict(y_k=y_k, y_v=y_v, kb=kb, vb=vb, h_last_k=hk, h_last_v=hv)
 

@@ -3,6 +3,9 @@
 // To Multi-Token States", "Core claim"; the selective SSM is the paper's Eq. 3, cited in
 // "Assumptions & free parameters").
 //
+// SSM_V may read its own input (the variant that keeps explicit key and value projections in
+// front of the SSMs); by default both SSMs read x, loaded once.
+//
 // Mapping on gfx950: one lane owns one channel c of both SSMs and keeps the 2*N state values
 // and the 2*N decay rates (A * log2 e) in VGPRs; a wave owns 64 consecutive channels and walks
 // a group of whole chunks token by token (chunks are independent because the state restarts
@@ -99,9 +102,11 @@ struct SsmLane {
   }
 };
 
-template <typename T, int N, int PU>
+// SEPX: SSM_V reads its own input xv (explicit key/value projections in front of the SSMs).
+template <typename T, int N, int PU, bool SEPX>
 __global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
     ScanShape sh, const int32_t* __restrict__ chunk_cu, const T* __restrict__ x,
+    const T* __restrict__ xv,
     const T* __restrict__ dtk, const T* __restrict__ dtv, const T* __restrict__ bmk,
     const T* __restrict__ cmk, const T* __restrict__ bmv, const T* __restrict__ cmv,
     const float* __restrict__ A_k, const float* __restrict__ A_v, const float* __restrict__ D_k,
@@ -147,39 +152,42 @@ __global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
     const int ce = chunk_cu[q + 1];
     float ok = 0.f, ov = 0.f;
     if (ce - cs == PU) {
-      float xs[PU], dks[PU], dvs[PU];
+      float xs[PU], xvs[PU], dks[PU], dvs[PU];
 #pragma unroll
       for (int j = 0; j < PU; ++j) {
         const int o = (cs + j) * d + c;
         xs[j] = to_f32(x[o]); dks[j] = to_f32(dtk[o]); dvs[j] = to_f32(dtv[o]);
+        xvs[j] = SEPX ? to_f32(xv[o]) : xs[j];
       }
 #pragma unroll
       for (int j = 0; j < PU; ++j) {
         const int t = cs + j;
         if (j == 0) {
           ok = sk.template step<true>(xs[j], dks[j], bmk + t * N, cmk + t * N);
-          ov = sv.template step<true>(xs[j], dvs[j], bmv + t * N, cmv + t * N);
+          ov = sv.template step<true>(xvs[j], dvs[j], bmv + t * N, cmv + t * N);
         } else {
           ok = sk.template step<false>(xs[j], dks[j], bmk + t * N, cmk + t * N);
-          ov = sv.template step<false>(xs[j], dvs[j], bmv + t * N, cmv + t * N);
+          ov = sv.template step<false>(xvs[j], dvs[j], bmv + t * N, cmv + t * N);
         }
         yk[t * d + c] = from_f32<T>(ok);
         yv[t * d + c] = from_f32<T>(ov);
       }
     } else {
       float nx = to_f32(x[cs * d + c]), ndk = to_f32(dtk[cs * d + c]), ndv = to_f32(dtv[cs * d + c]);
+      float nxv = SEPX ? to_f32(xv[cs * d + c]) : nx;
       for (int t = cs; t < ce; ++t) {
-        const float xv = nx, dk = ndk, dv = ndv;
+        const float xk_t = nx, xv_t = nxv, dk = ndk, dv = ndv;
         if (t + 1 < ce) {
           const int o = (t + 1) * d + c;
           nx = to_f32(x[o]); ndk = to_f32(dtk[o]); ndv = to_f32(dtv[o]);
+          nxv = SEPX ? to_f32(xv[o]) : nx;
         }
         if (t == cs) {
-          ok = sk.template step<true>(xv, dk, bmk + t * N, cmk + t * N);
-          ov = sv.template step<true>(xv, dv, bmv + t * N, cmv + t * N);
+          ok = sk.template step<true>(xk_t, dk, bmk + t * N, cmk + t * N);
+          ov = sv.template step<true>(xv_t, dv, bmv + t * N, cmv + t * N);
         } else {
-          ok = sk.template step<false>(xv, dk, bmk + t * N, cmk + t * N);
-          ov = sv.template step<false>(xv, dv, bmv + t * N, cmv + t * N);
+          ok = sk.template step<false>(xk_t, dk, bmk + t * N, cmk + t * N);
+          ov = sv.template step<false>(xv_t, dv, bmv + t * N, cmv + t * N);
         }
         yk[t * d + c] = from_f32<T>(ok);
         yv[t * d + c] = from_f32<T>(ov);
@@ -190,11 +198,12 @@ __global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
   }
 }
 
-template <typename T, int N>
+template <typename T, int N, bool SEPX>
 hipError_t launch_typed(const attamba_scan_args& a, const ScanShape& sh, hipStream_t stream) {
   const int blocks = ceil_div(sh.groups, 8) * 8 * sh.ctiles;
-  hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8>), dim3(blocks), dim3(kWave), 0, stream, sh,
-                     a.chunk_cu, static_cast<const T*>(a.x), static_cast<const T*>(a.dt_k),
+  hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, SEPX>), dim3(blocks), dim3(kWave), 0, stream, sh,
+                     a.chunk_cu, static_cast<const T*>(a.x), static_cast<const T*>(a.x_v),
+                     static_cast<const T*>(a.dt_k),
                      static_cast<const T*>(a.dt_v), static_cast<const T*>(a.bm_k),
                      static_cast<const T*>(a.cm_k), static_cast<const T*>(a.bm_v),
                      static_cast<const T*>(a.cm_v), a.A_k, a.A_v, a.D_k, a.D_v, a.bias_k,
@@ -212,10 +221,13 @@ hipError_t launch_kvssm_scan(const attamba_scan_args& a, hipStream_t stream) {
   sh.T = a.T; sh.d = a.d; sh.n_chunks = a.n_chunks; sh.S = a.S;
   sh.groups = ceil_div(a.n_chunks, kChunksPerWave);
   sh.ctiles = a.d / kWave;
+  const bool sep = a.x_v != nullptr && a.x_v != a.x;
   if (a.dtype == ATTAMBA_BF16) {
-    return a.N == 16 ? launch_typed<__bf16, 16>(a, sh, stream) : launch_typed<__bf16, 32>(a, sh, stream);
+    if (sep) return a.N == 16 ? launch_typed<__bf16, 16, true>(a, sh, stream) : launch_typed<__bf16, 32, true>(a, sh, stream);
+    return a.N == 16 ? launch_typed<__bf16, 16, false>(a, sh, stream) : launch_typed<__bf16, 32, false>(a, sh, stream);
   }
-  return a.N == 16 ? launch_typed<float, 16>(a, sh, stream) : launch_typed<float, 32>(a, sh, stream);
+  if (sep) return a.N == 16 ? launch_typed<float, 16, true>(a, sh, stream) : launch_typed<float, 32, true>(a, sh, stream);
+  return a.N == 16 ? launch_typed<float, 16, false>(a, sh, stream) : launch_typed<float, 32, false>(a, sh, stream);
 }
 
 }  // namespace attamba

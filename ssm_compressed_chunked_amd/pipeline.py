@@ -50,7 +50,7 @@ def prefill_forward(act: dict, params: dict, seq_cu_host, H: int, hd: int, P: in
     scan = B.kvssm_scan(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"],
                         act["bm_v"], act["cm_v"], params["A_k"], params["A_v"], params["D_k"],
                         params["D_v"], params["bias_k"], params["bias_v"], layout.chunk_cu,
-                        stream=stream)
+                        x_v=act.get("x_v"), stream=stream)
     max_len = int(np.max(np.diff(seq_cu_host))) if len(seq_cu_host) > 1 else 0
     n = layout.n_chunks
     out, lse = B.chunk_attn_fwd(act["q"].view(T, H, hd), scan["y_k"].view(T, H, hd),
@@ -66,15 +66,26 @@ PROJ_NAMES = ("q", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v")
 
 def layer_forward(x: torch.Tensor, w_stack: torch.Tensor, params: dict, seq_cu_host, H: int,
                   hd: int, N: int, P: int | None, layer_idx: int, L: int, mode: int,
-                  chunk_lens=None, stream=None, want_lse: bool = True) -> dict:
+                  chunk_lens=None, stream=None, want_lse: bool = True,
+                  explicit_kv: bool = False) -> dict:
     """One layer from its input: x [T, d] (bf16) and the stacked projection weight w_stack
     [3 d + 4 N, d] (rows: q, dt_K, dt_V, Bm_K, Cm_K, Bm_V, Cm_V) -> the input projections on the
     matrix cores, then the KV-SSM forward of `prefill_forward`. The layer index sets the cyclic
-    chunk offset, so consecutive layers of a model use shifted chunk boundaries."""
+    chunk offset, so consecutive layers of a model use shifted chunk boundaries.
+
+    explicit_kv: the variant that keeps key and value projections in front of the SSMs; w_stack
+    then has 5 d + 4 N rows (q, x_K, x_V, dt_K, dt_V, Bm_K, Cm_K, Bm_V, Cm_V), the SSMs read
+    x_K = x W_K and x_V = x W_V, and the dt/Bm/Cm rows are the SSM projections composed with
+    W_K or W_V (a product of two linear maps is one linear map of x)."""
     T, d = x.shape
-    outs = B.input_proj(x, w_stack, [d, d, d, N, N, N, N], stream=stream)
-    act = dict(zip(PROJ_NAMES, outs))
-    act["x"] = x
+    if explicit_kv:
+        names = ("q", "x", "x_v", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v")
+        outs = B.input_proj(x, w_stack, [d, d, d, d, d, N, N, N, N], stream=stream)
+        act = dict(zip(names, outs))
+    else:
+        outs = B.input_proj(x, w_stack, [d, d, d, N, N, N, N], stream=stream)
+        act = dict(zip(PROJ_NAMES, outs))
+        act["x"] = x
     res = prefill_forward(act, params, seq_cu_host, H, hd, P, layer_idx, L, mode,
                           chunk_lens=chunk_lens, stream=stream, want_lse=want_lse)
     res["proj"] = act

@@ -121,7 +121,7 @@ def test_input_proj_validates_before_launch():
     a.seg_start[2] = 20
     assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # does not reach n_out
     a.seg_start[2] = 24
-    a.n_seg = 9
+    a.n_seg = B.PROJ_MAX_SEGMENTS + 1
     assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # too many segments
     a.n_seg = 2
     assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_NULL_ARG       # x, w, out null

@@ -429,24 +429,32 @@ def test_input_proj_full_size_sampled():
         start += wd
 
 
-@pytest.mark.parametrize("layer", [0, 3, 6])
-def test_layer_forward_from_x(layer):
+@pytest.mark.parametrize("layer,explicit_kv", [(0, False), (3, False), (6, False), (1, True)])
+def test_layer_forward_from_x(layer, explicit_kv):
     """Projections on the matrix cores feeding the KV-SSM forward, for three layers whose
     chunk boundaries are shifted by the layer index. The oracle projects in float64 and rounds
     to bf16 with round-to-nearest-even, the storage type the GPU path hands to the scan."""
     T, d, H, hd, N, P, L = 330, 128, 2, 64, 16, 4, 5
-    say(f"layer forward layer={layer}")
+    say(f"layer forward layer={layer} explicit_kv={explicit_kv}")
     pj = make_projection(T, d, N, seed=40 + layer)
+    names = ["q", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v"]
+    widths = [d, d, d, N, N, N, N]
+    if explicit_kv:   # two more weight blocks: the key and value projections
+        rng = np.random.default_rng(50 + layer)
+        extra = torch.from_numpy(rng.standard_normal((2 * d, d)).astype(np.float32) * 0.05).to(torch.bfloat16)
+        pj.w = torch.cat([pj.w[:d], extra, pj.w[d:]])
+        names = ["q", "x", "x_v"] + names[1:]
+        widths = [d, d, d] + widths[1:]
     par = make_prefill(PREFILL_BF16.with_(B=1, n=T, d=d, H=H, hd=hd, N=N), seed=41).param
     seq_cu = np.array([0, 200, T], dtype=np.int32)
     res = layer_forward(pj.x.cuda(), pj.w.cuda(), {k: v.cuda() for k, v in par.items()}, seq_cu,
-                        H, hd, N, P, layer, L, att.MASK_TEST)
+                        H, hd, N, P, layer, L, att.MASK_TEST, explicit_kv=explicit_kv)
     torch.cuda.synchronize()
     proj = oracle.linear(pj.x.double().numpy(), pj.w.double().numpy())
     proj = torch.from_numpy(proj).to(torch.bfloat16).double().numpy()   # storage rounding
     f = {"x": pj.x.double().numpy()}
     start = 0
-    for name, wd in zip(("q", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v"), [d, d, d, N, N, N, N]):
+    for name, wd in zip(names, widths):
         f[name] = proj[:, start:start + wd]
         start += wd
     for k, v in par.items():
@@ -455,3 +463,24 @@ def test_layer_forward_from_x(layer):
     np.testing.assert_array_equal(res["layout"].chunk_cu.cpu().numpy(), ref["chunk_cu"])
     check_close(res["scan"]["y_k"].float().cpu().numpy(), ref["y_k"], "bf16", "y_k")
     check_close(res["out"].float().cpu().numpy(), ref["out"], "bf16", "out")
+
+
+def test_scan_separate_value_input():
+    """SSM_V on its own input (explicit value projection kept in front of the SSM): y_K is the
+    usual result, y_V follows x_v."""
+    cfg = PREFILL_BF16.with_(B=2, n=150, d=128, H=2, P=8, L=4)
+    inp = make_prefill(cfg, seed=31)
+    rng = np.random.default_rng(31)
+    xv = torch.from_numpy(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)).to(torch.bfloat16)
+    act, par = to_dev(inp)
+    lay = chunk_layout(inp.seq_cu, torch.from_numpy(inp.seq_cu).cuda(), cfg.T, cfg.P, 0)
+    res = att.kvssm_scan(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"], act["bm_v"],
+                         act["cm_v"], par["A_k"], par["A_v"], par["D_k"], par["D_v"], par["bias_k"],
+                         par["bias_v"], lay.chunk_cu, x_v=xv.cuda())
+    torch.cuda.synchronize()
+    f = f64_inputs(inp)
+    f["x_v"] = xv.double().numpy()
+    ref = oracle.kvssm_forward(f, inp.seq_cu, cfg.H, cfg.hd, cfg.P, 0, cfg.L, "test")
+    check_close(res["y_k"].float().cpu().numpy(), ref["y_k"], "bf16", "y_k")
+    check_close(res["y_v"].float().cpu().numpy(), ref["y_v"], "bf16", "y_v")
+    check_close(res["vb"].float().cpu().numpy().reshape(-1, cfg.H, cfg.hd), ref["vb"], "bf16", "vb")
