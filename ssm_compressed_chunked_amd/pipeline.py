@@ -90,3 +90,47 @@ def layer_forward(x: torch.Tensor, w_stack: torch.Tensor, params: dict, seq_cu_h
                           chunk_lens=chunk_lens, stream=stream, want_lse=want_lse)
     res["proj"] = act
     return res
+
+
+def chunk_ends_before(n: int, P: int, layer_idx: int) -> int:
+    """Chunk ends among positions 0 .. n-1 under the positional rule (position j ends a chunk
+    iff (j + 1 - o) mod P == 0, o = layer_idx mod P): the boundary states a decode cache holds
+    after n tokens."""
+    o = layer_idx % P
+    if n <= 0:
+        return 0
+    if o == 0:
+        return n // P
+    return (n - o) // P + 1 if n >= o else 0
+
+
+def kv_footprint(n: int, P: int, L: int, H: int, hd: int, N: int, layer_idx: int = 0,
+                 dtype_bytes: int = 2, P_baseline: int | None = None) -> dict:
+    """Per layer and sequence after n tokens (pith.science Referee Report, first major comment;
+    "If this is right": the cache shrinks by about P):
+      attamba_states   cached boundary states + window entries (n/P + L at P | n)
+      attended         keys the next query attends to (boundaries before its window + window)
+      attamba_bytes    those K/V entries plus the two fp32 SSM states [d, N]
+      dense_bytes      a transformer's full K/V cache of n entries
+      iso_kv_bytes     the footprint-matched transformer of the review: head dim E/P, all n
+      swa_window       that baseline's sliding window at evaluation, L/P
+    P_baseline: the chunk size used for the baseline's reductions (default P)."""
+    E = H * hd
+    Pb = P if P_baseline is None else P_baseline
+    n_bound = chunk_ends_before(n, P, layer_idx)
+    window = min(L, n)
+    w = max(0, n - L + 1) if L > 0 else n + 1          # window of the query at position n
+    attended = chunk_ends_before(w, P, layer_idx) + (n - w + 1 if L > 0 else 0)
+    kv = 2 * E * dtype_bytes
+    return dict(n=n, attamba_states=n_bound + window, attended=attended,
+                attamba_bytes=(n_bound + window) * kv + 2 * E * N * 4,
+                dense_bytes=n * kv, iso_kv_bytes=n * 2 * (E // Pb) * dtype_bytes,
+                swa_window=L // Pb, compression=n / max(n_bound + window, 1))
+
+
+def decode_cache_bytes(cache) -> int:
+    """Device bytes a DecodeCache holds (capacity-sized boundary cache, window, states,
+    workspace)."""
+    return sum(t.numel() * t.element_size()
+               for t in (cache.kb, cache.vb, cache.kw, cache.vw, cache.h_k, cache.h_v,
+                         cache.workspace))
