@@ -1,4 +1,5 @@
-"""Plain, slow CPU oracle of Attamba's KV-SSM forward, chunk-aware attention and decode.
+"""Plain, slow CPU oracle of Attamba's KV-SSM forward, chunk-aware attention and decode, and
+the reverse-mode gradients of the scan and of the attention (training with M_train).
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link this module:
 only the tests, the smoke check and the CPU-baseline leg of the benchmark use it. It shares
@@ -25,6 +26,8 @@ notes of the repository):
     (j ends a chunk, or (M_train and j is in i's chunk), or i - j < L). This is the causal
     reading of M_test: the current chunk's boundary is visible only once it is complete.
   * A query row with no visible key gives O = 0 and LSE = -inf.
+  * Backward: the gradients are those of the forward above, by the chain rule (reverse mode);
+    they are pinned against central finite differences of this module's forward.
 """
 from __future__ import annotations
 
@@ -144,6 +147,60 @@ def selective_scan(x, dt, dt_bias, A, Bm, Cm, D, chunk_cu, t_begin: int = 0,
     return y, snaps
 
 
+def selective_scan_backward(x, dt, dt_bias, A, Bm, Cm, D, chunk_cu, gy):
+    """Gradients of sum(gy * y) for y = selective_scan(x, dt, dt_bias, A, Bm, Cm, D, chunk_cu)
+    over all tokens: reverse mode of the recurrence, token by token backwards within each chunk
+    (the state restarts at every chunk start, so no gradient crosses a chunk start).
+
+    Returns dict(dx [T, d], ddt [T, d], dbias [d], dA [d, N], dBm [T, N], dCm [T, N], dD [d]).
+    """
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    A = np.asarray(A, np.float64)
+    D = np.asarray(D, np.float64)
+    Bm = np.asarray(Bm, np.float64)
+    Cm = np.asarray(Cm, np.float64)
+    gy = np.asarray(gy, np.float64)
+    z = np.asarray(dt, np.float64) + np.asarray(dt_bias, np.float64)
+    delta = softplus(z)
+    sig = 1.0 / (1.0 + np.exp(-z))             # derivative of softplus
+    starts = set(int(v) for v in chunk_cu[:-1])
+    # forward, keeping every state
+    hs = np.zeros((T, d, A.shape[1]))
+    h = np.zeros_like(A)
+    for t in range(T):
+        if t in starts:
+            h = np.zeros_like(A)
+        h = np.exp(delta[t][:, None] * A) * h + (delta[t] * x[t])[:, None] * Bm[t][None, :]
+        hs[t] = h
+    g = dict(dx=np.zeros((T, d)), ddt=np.zeros((T, d)), dbias=np.zeros(d),
+             dA=np.zeros_like(A), dBm=np.zeros_like(Bm), dCm=np.zeros_like(Cm), dD=np.zeros(d))
+    cu = [int(v) for v in chunk_cu]
+    for a, b in zip(cu[:-1], cu[1:]):
+        dh = np.zeros_like(A)                  # gradient with respect to the state after t
+        for t in range(b - 1, a - 1, -1):
+            # y_t = Cm_t . h_t + D x_t
+            g["dD"] += gy[t] * x[t]
+            g["dx"][t] += gy[t] * D
+            g["dCm"][t] += gy[t] @ hs[t]
+            dh = dh + gy[t][:, None] * Cm[t][None, :]
+            # h_t = exp(delta_t A) h_{t-1} + (delta_t x_t) Bm_t
+            e = np.exp(delta[t][:, None] * A)
+            u = delta[t] * x[t]
+            hprev = hs[t - 1] if t > a else np.zeros_like(A)
+            g["dBm"][t] += (dh * u[:, None]).sum(axis=0)
+            du = (dh * Bm[t][None, :]).sum(axis=1)
+            de = dh * hprev
+            ddelta = du * x[t] + (de * e * A).sum(axis=1)
+            g["dx"][t] += du * delta[t]
+            g["dA"] += de * e * delta[t][:, None]
+            dz = ddelta * sig[t]
+            g["ddt"][t] += dz
+            g["dbias"] += dz
+            dh = dh * e
+    return g
+
+
 def boundary_states(y, chunk_cu):
     """One state per chunk: the SSM output at the chunk's last token (the review's
     K^(p)[-1]: "the SSM output after processing the entire chunk")."""
@@ -195,6 +252,52 @@ def masked_attention(q, k, v, mask, scale: float):
         out[live, h, :] = (p[live] @ v[:, h, :]) / denom[live, None]
         lse[h, live] = mx[live] + np.log(denom[live])
     return out, lse
+
+
+def masked_attention_backward(q, k, v, mask, scale: float, dout):
+    """Gradients of sum(dout * O) for O = masked_attention(q, k, v, mask, scale): the softmax
+    rows, dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dP P)), dQ = scale dS K,
+    dK = scale dS^T Q. Rows with no visible key pass no gradient. Returns dq, dk, dv."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    live = mask.any(axis=1)
+    for h in range(q.shape[1]):
+        s = (q[:, h, :] @ k[:, h, :].T) * scale
+        s = np.where(mask, s, -np.inf)
+        mx = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
+        p = np.exp(s - mx[:, None])
+        p[live] /= p[live].sum(axis=1, keepdims=True)
+        dv[:, h, :] = p.T @ dout[:, h, :]
+        dp = dout[:, h, :] @ v[:, h, :].T
+        ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+        dq[:, h, :] = scale * (ds @ k[:, h, :])
+        dk[:, h, :] = scale * (ds.T @ q[:, h, :])
+    return dq, dk, dv
+
+
+def chunk_attention_backward(q, k, v, seq_cu, token_chunk, is_end, L: int, mode: str, dout,
+                             scale: float | None = None):
+    """Gradients of sum(dout * O) for O = chunk_attention(...) over a packed batch: dq, dk, dv
+    [T, H, hd]. dk and dv are the total gradients of the per-token keys and values, through
+    their use as window keys and as boundary states alike (one position, one key)."""
+    T, H, hd = np.shape(q)
+    scale = 1.0 / math.sqrt(hd) if scale is None else scale
+    seq_cu = np.asarray(seq_cu, dtype=np.int64)
+    dq = np.zeros((T, H, hd))
+    dk = np.zeros((T, H, hd))
+    dv = np.zeros((T, H, hd))
+    for b in range(len(seq_cu) - 1):
+        s0, s1 = int(seq_cu[b]), int(seq_cu[b + 1])
+        if s1 <= s0:
+            continue
+        mask = dense_mask(np.asarray(token_chunk)[s0:s1], np.asarray(is_end)[s0:s1], L, mode)
+        a, bk, c = masked_attention_backward(q[s0:s1], k[s0:s1], v[s0:s1], mask, scale,
+                                             dout[s0:s1])
+        dq[s0:s1], dk[s0:s1], dv[s0:s1] = a, bk, c
+    return dq, dk, dv
 
 
 def chunk_attention(q, k, v, seq_cu, token_chunk, is_end, L: int, mode: str,

@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "attamba_oracle.py")
 PINS = ["test_oracle_segment.py", "test_oracle_scan.py", "test_oracle_attention.py",
-        "test_oracle_decode.py", "test_oracle_proj.py"]
+        "test_oracle_decode.py", "test_oracle_proj.py", "test_oracle_backward.py"]
 
 MUTANTS = [
     ("decay uses the previous step size", "decay = np.exp(delta[k][:, None] * A)",
@@ -51,6 +51,14 @@ MUTANTS = [
     ("projection with a dropped input feature", "return x @ w.T", "return x[:, 1:] @ w[:, 1:].T"),
     ("first chunk not shortened by the offset", "return [t for t in range(n) if t == 0 or (t - o) % P == 0]",
      "return [t for t in range(n) if t % P == 0]"),
+    ("backward state gradient not decayed", "            dh = dh * e\n", "            pass\n"),
+    ("backward softmax without the row term", "ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))",
+     "ds = p * dp"),
+    ("backward softplus derivative dropped", "dz = ddelta * sig[t]", "dz = ddelta"),
+    ("backward dA without the step size", "g[\"dA\"] += de * e * delta[t][:, None]",
+     "g[\"dA\"] += de * e"),
+    ("backward key gradient from dS instead of dS^T", "dk[:, h, :] = scale * (ds.T @ q[:, h, :])",
+     "dk[:, h, :] = scale * (ds @ q[:, h, :])"),
 ]
 
 
