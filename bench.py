@@ -9,6 +9,7 @@ N=16, P=8, L=64, uniform chunks, M_test + window). Prints one JSON line.
     python bench.py --workload decode_bf16      # decode configuration, separate line
     python bench.py --workload proj_bf16        # input projections (x W^T) at the prefill shape
     python bench.py --workload layer_bf16       # projections + KV-SSM forward from the layer input
+    python bench.py --workload train_step_bf16  # forward + backward at the M_train workload
     python bench.py --workload copy             # reference bandwidth (512 MiB device copy)
 """
 from __future__ import annotations
@@ -424,6 +425,60 @@ def bench_layer(args):
                    "head_dim": hd, "N": N, "P": cfg.P, "L": cfg.L}}), flush=True)
 
 
+def bench_train(args):
+    """One training step of the KV-SSM path at the M_train workload (bf16, B=4, n=2048,
+    d=1024, 16 heads x 64, N=16, P=8, L=64, layer 3): segmentation, both scans, the attention
+    with its LSE, then the attention backward and the scan backward for a seeded output
+    gradient. Phase times come from HIP events on the launch stream."""
+    import torch
+    import ssm_compressed_chunked_amd as att
+    from ssm_compressed_chunked_amd.pipeline import prefill_backward, prefill_forward
+    from workloads import PREFILL_CONFIGS, make_output_grad, make_prefill
+    cfg = PREFILL_CONFIGS["train_bf16"]
+    T, H, hd = cfg.T, cfg.H, cfg.hd
+    inp = make_prefill(cfg)
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    par = {k: v.cuda() for k, v in inp.param.items()}
+    act["seq_cu"] = torch.from_numpy(inp.seq_cu).cuda()
+    dout = make_output_grad((T, H, hd), cfg.dtype, seed=42).cuda()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    phase = np.zeros(2)
+
+    def step(record=False):
+        if record:
+            ev[0].record(stream)
+        res = prefill_forward(act, par, inp.seq_cu, H, hd, cfg.P, cfg.layer_idx, cfg.L,
+                              att.MASK_TRAIN, stream=stream)
+        if record:
+            ev[1].record(stream)
+        prefill_backward(res, act, par, dout, H, hd, cfg.L, att.MASK_TRAIN, stream=stream)
+        if record:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+        ev[2].synchronize()
+        phase += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(json.dumps({
+        "metric": "tokens/sec, KV-SSM forward + backward (training step)",
+        "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "phases_ms": {"forward": round(phase[0] / args.steps, 4),
+                      "backward": round(phase[1] / args.steps, 4)},
+        "config": {"workload": "train_step_bf16", "B": cfg.B, "n": cfg.n, "d_model": cfg.d,
+                   "heads": H, "head_dim": hd, "N": cfg.N, "P": cfg.P, "L": cfg.L,
+                   "layer_idx": cfg.layer_idx, "mask": "M_train"}}), flush=True)
+
+
 def bench_copy(args):
     """A plain device copy of 512 MiB: the reference point that scales rocprofv3's FETCH_SIZE
     and WRITE_SIZE counters to bytes (the copy moves exactly 512 MiB each way per launch)."""
@@ -468,6 +523,8 @@ def main():
         bench_proj(args)
     elif args.workload == "layer_bf16":
         bench_layer(args)
+    elif args.workload == "train_step_bf16":
+        bench_train(args)
     elif args.workload.startswith("decode"):
         bench_decode(args)
     else:

@@ -280,6 +280,72 @@ typedef struct {
 
 int attamba_input_proj(const attamba_proj_args* args, attamba_stream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Backward pass (training). The pages' results are models trained end to end (pith.science
+ * "Core claim" and the Referee Report's summary: about 60M parameters, 1B or 8B tokens), with
+ * the M_train mask at training time ("What carries the argument", Eq. 5). These two calls
+ * give the reverse-mode gradients of
+ * attamba_chunk_attn_fwd and attamba_kvssm_scan for a given gradient of their outputs.
+ * Gradient sums over tokens or channels use float atomics: results are reproducible up to
+ * float reassociation, not bit for bit.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Attention backward. fwd holds the forward call's arguments unchanged (sizes, inputs q, k, v,
+ * kb, vb, index arrays, mask); fwd.out and fwd.lse must hold that call's results (lse is
+ * required). With P the softmax weights and D_i = dout_i . out_i:
+ *   dq_i = scale sum_j P_ij (dout_i . v_j - D_i) k_j over the keys row i sees, and for each key
+ *   dk_j = scale sum_i P_ij (dout_i . v_j - D_i) q_i, dv_j = sum_i P_ij dout_i over the rows
+ *   that see it. A key position reached through the compact boundary states (rows whose band
+ *   starts after it) contributes to dkb/dvb; reached as a per-token key (rows whose band holds
+ *   it), to dk/dv. The total gradient of the per-token SSM output at a chunk's last token is
+ *   dk plus that chunk's dkb (attamba_kvssm_scan_bwd adds them when given gkb/gvb).
+ * All gradients are written in fwd.dtype; every element of dq, dk, dv, dkb, dvb is written.
+ * Errors: as attamba_chunk_attn_fwd, plus NULL_ARG for lse, dout, a gradient or workspace. */
+typedef struct {
+  attamba_attn_args fwd;
+  const void* dout;    /* [T, H, hd] gradient of out */
+  void* dq;            /* [T, H, hd] out */
+  void* dk;            /* [T, H, hd] out: gradient of k */
+  void* dv;            /* [T, H, hd] out: gradient of v */
+  void* dkb;           /* [n_chunks, H, hd] out: gradient of kb */
+  void* dvb;           /* [n_chunks, H, hd] out: gradient of vb */
+  float* workspace;    /* [H, T] device scratch, float32 */
+} attamba_attn_bwd_args;
+
+int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* args, attamba_stream_t stream);
+
+/* KV-SSM scan backward. fwd holds the forward call's arguments (only its inputs are read; its
+ * outputs may be NULL). Given the gradients of y_k, y_v (and optionally of kb, vb, added at each
+ * chunk's last token), writes per SSM S in {K, V}:
+ *   dx_S   gradient of S's input through S (x for SSM_K; x_v, or x when x_v is NULL, for SSM_V):
+ *          when both SSMs read x, the gradient of x is dx_k + dx_v;
+ *   ddt_S  gradient of the step-size pre-activation dt_S;
+ *   dbm_S, dcm_S [T, N], dA_S [d, N], dD_S, dbias_S [d]: float32, summed over channels / tokens.
+ * Errors: as attamba_kvssm_scan, plus NULL_ARG for a missing gradient pointer. */
+typedef struct {
+  attamba_scan_args fwd;
+  const void* gy_k;    /* [T, d] gradient of y_k */
+  const void* gy_v;    /* [T, d] gradient of y_v */
+  const void* gkb;     /* [n_chunks, d] gradient of kb, or NULL (zero) */
+  const void* gvb;     /* [n_chunks, d] gradient of vb, or NULL */
+  void* dx_k;          /* [T, d] out */
+  void* dx_v;          /* [T, d] out */
+  void* ddt_k;         /* [T, d] out */
+  void* ddt_v;         /* [T, d] out */
+  float* dbm_k;        /* [T, N] out */
+  float* dcm_k;        /* [T, N] out */
+  float* dbm_v;        /* [T, N] out */
+  float* dcm_v;        /* [T, N] out */
+  float* dA_k;         /* [d, N] out */
+  float* dA_v;         /* [d, N] out */
+  float* dD_k;         /* [d] out */
+  float* dD_v;         /* [d] out */
+  float* dbias_k;      /* [d] out */
+  float* dbias_v;      /* [d] out */
+} attamba_scan_bwd_args;
+
+int attamba_kvssm_scan_bwd(const attamba_scan_bwd_args* args, attamba_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

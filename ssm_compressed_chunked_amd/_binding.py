@@ -52,6 +52,18 @@ class AttnArgs(C.Structure):
                 ("out", _vp), ("lse", _vp)]
 
 
+class AttnBwdArgs(C.Structure):
+    _fields_ = [("fwd", AttnArgs), ("dout", _vp), ("dq", _vp), ("dk", _vp), ("dv", _vp),
+                ("dkb", _vp), ("dvb", _vp), ("workspace", _vp)]
+
+
+class ScanBwdArgs(C.Structure):
+    _fields_ = [("fwd", ScanArgs), ("gy_k", _vp), ("gy_v", _vp), ("gkb", _vp), ("gvb", _vp),
+                ("dx_k", _vp), ("dx_v", _vp), ("ddt_k", _vp), ("ddt_v", _vp), ("dbm_k", _vp),
+                ("dcm_k", _vp), ("dbm_v", _vp), ("dcm_v", _vp), ("dA_k", _vp), ("dA_v", _vp),
+                ("dD_k", _vp), ("dD_v", _vp), ("dbias_k", _vp), ("dbias_v", _vp)]
+
+
 class DecodeCacheStruct(C.Structure):
     _fields_ = [("B", _i32), ("H", _i32), ("hd", _i32), ("d", _i32), ("N", _i32), ("P", _i32),
                 ("L", _i32), ("layer_idx", _i32), ("cap", _i32), ("dtype", _i32),
@@ -81,6 +93,8 @@ EXPORTS = {
                                       C.c_int),
     "attamba_decode_step": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodeInputsStruct), _vp],
                             C.c_int),
+    "attamba_chunk_attn_bwd": ([C.POINTER(AttnBwdArgs), _vp], C.c_int),
+    "attamba_kvssm_scan_bwd": ([C.POINTER(ScanBwdArgs), _vp], C.c_int),
 }
 
 _lib = None
@@ -198,6 +212,26 @@ def chunk_index(chunk_cu: torch.Tensor, T: int, token_chunk=None, is_end=None, s
     return token_chunk, is_end
 
 
+def _scan_inputs(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k, bias_v,
+                 chunk_cu, x_v) -> ScanArgs:
+    """ScanArgs with the sizes and the forward inputs filled in (outputs left NULL)."""
+    T, d = x.shape
+    N = A_k.shape[1]
+    act = x.dtype
+    a = ScanArgs()
+    a.T, a.d, a.N, a.dtype, a.n_chunks = T, d, N, _dtype_code(x), chunk_cu.numel() - 1
+    a.chunk_cu = _dev(chunk_cu, "chunk_cu", torch.int32)
+    for name, t, n in (("x", x, T * d), ("dt_k", dt_k, T * d), ("dt_v", dt_v, T * d),
+                       ("bm_k", bm_k, T * N), ("cm_k", cm_k, T * N), ("bm_v", bm_v, T * N),
+                       ("cm_v", cm_v, T * N)):
+        setattr(a, name, _dev(t, name, act, n))
+    for name, t, n in (("A_k", A_k, d * N), ("A_v", A_v, d * N), ("D_k", D_k, d),
+                       ("D_v", D_v, d), ("bias_k", bias_k, d), ("bias_v", bias_v, d)):
+        setattr(a, name, _dev(t, name, torch.float32, n))
+    a.x_v = _dev(x_v, "x_v", act, T * d)
+    return a
+
+
 def kvssm_scan(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k, bias_v,
                chunk_cu, *, y_k=None, y_v=None, kb=None, vb=None, boundaries=True,
                seq_cu=None, h_last=False, x_v=None, stream=None) -> dict:
@@ -221,25 +255,50 @@ def kvssm_scan(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k
         S = seq_cu.numel() - 1
         hk = torch.empty((S, d, N), dtype=torch.float32, device=x.device)
         hv = torch.empty((S, d, N), dtype=torch.float32, device=x.device)
-    a = ScanArgs()
-    a.T, a.d, a.N, a.dtype, a.n_chunks = T, d, N, _dtype_code(x), n_chunks
-    a.chunk_cu = _dev(chunk_cu, "chunk_cu", torch.int32)
-    for name, t, n in (("x", x, T * d), ("dt_k", dt_k, T * d), ("dt_v", dt_v, T * d),
-                       ("bm_k", bm_k, T * N), ("cm_k", cm_k, T * N), ("bm_v", bm_v, T * N),
-                       ("cm_v", cm_v, T * N), ("y_k", y_k, T * d), ("y_v", y_v, T * d)):
-        setattr(a, name, _dev(t, name, act, n))
-    for name, t, n in (("A_k", A_k, d * N), ("A_v", A_v, d * N), ("D_k", D_k, d),
-                       ("D_v", D_v, d), ("bias_k", bias_k, d), ("bias_v", bias_v, d)):
-        setattr(a, name, _dev(t, name, torch.float32, n))
+    a = _scan_inputs(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k, bias_v,
+                     chunk_cu, x_v)
+    a.y_k = _dev(y_k, "y_k", act, T * d)
+    a.y_v = _dev(y_v, "y_v", act, T * d)
     a.kb = _dev(kb, "kb", act, n_chunks * d)
     a.vb = _dev(vb, "vb", act, n_chunks * d)
     a.seq_cu = _dev(seq_cu, "seq_cu", torch.int32) if h_last else None
     a.S = S
     a.h_last_k = _dev(hk, "h_last_k")
     a.h_last_v = _dev(hv, "h_last_v")
-    a.x_v = _dev(x_v, "x_v", act, T * d)
     _check(lib().attamba_kvssm_scan(C.byref(a), _stream(stream)))
     return dict(y_k=y_k, y_v=y_v, kb=kb, vb=vb, h_last_k=hk, h_last_v=hv)
+
+
+def kvssm_scan_bwd(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k, bias_v,
+                   chunk_cu, gy_k, gy_v, *, gkb=None, gvb=None, x_v=None, stream=None) -> dict:
+    """Gradients of both selective scans for the output gradients gy_k, gy_v [T, d] (and gkb,
+    gvb [n_chunks, d] of the boundary states). dx_k / dx_v are the gradients of each SSM's input
+    (when both read x, x's gradient is their sum). Returns a dict of the gradient tensors."""
+    T, d = x.shape
+    N = A_k.shape[1]
+    n_chunks = chunk_cu.numel() - 1
+    act = x.dtype
+    dev = x.device
+    b = ScanBwdArgs()
+    b.fwd = _scan_inputs(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k,
+                         bias_v, chunk_cu, x_v)
+    b.gy_k = _dev(gy_k, "gy_k", act, T * d)
+    b.gy_v = _dev(gy_v, "gy_v", act, T * d)
+    b.gkb = _dev(gkb, "gkb", act, n_chunks * d)
+    b.gvb = _dev(gvb, "gvb", act, n_chunks * d)
+    g = {}
+    for name in ("dx_k", "dx_v", "ddt_k", "ddt_v"):
+        g[name] = torch.empty((T, d), dtype=act, device=dev)
+    for name in ("dbm_k", "dcm_k", "dbm_v", "dcm_v"):
+        g[name] = torch.empty((T, N), dtype=torch.float32, device=dev)
+    for name in ("dA_k", "dA_v"):
+        g[name] = torch.empty((d, N), dtype=torch.float32, device=dev)
+    for name in ("dD_k", "dD_v", "dbias_k", "dbias_v"):
+        g[name] = torch.empty((d,), dtype=torch.float32, device=dev)
+    for name, t in g.items():
+        setattr(b, name, t.data_ptr())
+    _check(lib().attamba_kvssm_scan_bwd(C.byref(b), _stream(stream)))
+    return g
 
 
 def input_proj(x: torch.Tensor, w: torch.Tensor, widths, outs=None, stream=None):
@@ -268,17 +327,12 @@ def input_proj(x: torch.Tensor, w: torch.Tensor, widths, outs=None, stream=None)
     return outs
 
 
-def chunk_attn_fwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: int, L: int,
-                   mode: int, scale: float = 0.0, out=None, lse=None, return_lse: bool = True,
-                   stream=None):
-    """q, k, v: [T, H, hd]; kb, vb: [n_chunks, H, hd]. Returns (out, lse or None)."""
+def _attn_inputs(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen, L, mode,
+                 scale) -> AttnArgs:
+    """AttnArgs with sizes, mask and inputs filled in (out and lse left NULL)."""
     T, H, hd = q.shape
     n_chunks = chunk_cu.numel() - 1
     act = q.dtype
-    if out is None:
-        out = torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     a = AttnArgs()
     a.T, a.H, a.hd, a.dtype = T, H, hd, _dtype_code(q)
     a.S, a.max_seqlen, a.n_chunks, a.L, a.mode = seq_cu.numel() - 1, max_seqlen, n_chunks, L, mode
@@ -291,10 +345,52 @@ def chunk_attn_fwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: i
     a.seq_cu = _dev(seq_cu, "seq_cu", torch.int32)
     a.chunk_cu = _dev(chunk_cu, "chunk_cu", torch.int32)
     a.token_chunk = _dev(token_chunk, "token_chunk", torch.int32, T)
+    return a
+
+
+def chunk_attn_fwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: int, L: int,
+                   mode: int, scale: float = 0.0, out=None, lse=None, return_lse: bool = True,
+                   stream=None):
+    """q, k, v: [T, H, hd]; kb, vb: [n_chunks, H, hd]. Returns (out, lse or None)."""
+    T, H, hd = q.shape
+    n_chunks = chunk_cu.numel() - 1
+    act = q.dtype
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    a = _attn_inputs(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen, L, mode, scale)
     a.out = _dev(out, "out", act, T * H * hd)
     a.lse = _dev(lse, "lse", torch.float32, H * T) if lse is not None else None
     _check(lib().attamba_chunk_attn_fwd(C.byref(a), _stream(stream)))
     return out, lse
+
+
+def chunk_attn_bwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: int, L: int,
+                   mode: int, out, lse, dout, scale: float = 0.0, workspace=None,
+                   stream=None) -> dict:
+    """Gradients of the chunk attention for the output gradient dout, given the forward's
+    out and lse. Returns dict(dq, dk, dv, dkb, dvb): dk/dv for the per-token keys and values,
+    dkb/dvb for the boundary states."""
+    T, H, hd = q.shape
+    n_chunks = chunk_cu.numel() - 1
+    act = q.dtype
+    b = AttnBwdArgs()
+    b.fwd = _attn_inputs(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen, L, mode,
+                         scale)
+    b.fwd.out = _dev(out, "out", act, T * H * hd)
+    b.fwd.lse = _dev(lse, "lse", torch.float32, H * T)
+    b.dout = _dev(dout, "dout", act, T * H * hd)
+    if workspace is None:
+        workspace = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    b.workspace = _dev(workspace, "workspace", torch.float32, H * T)
+    g = dict(dq=torch.empty_like(q), dk=torch.empty_like(q), dv=torch.empty_like(q),
+             dkb=torch.empty((n_chunks, H, hd), dtype=act, device=q.device),
+             dvb=torch.empty((n_chunks, H, hd), dtype=act, device=q.device))
+    for name, t in g.items():
+        setattr(b, name, t.data_ptr())
+    _check(lib().attamba_chunk_attn_bwd(C.byref(b), _stream(stream)))
+    return g
 
 
 class DecodeCache:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattamba.so")
 SOURCES = ["boundaries.hip", "kvssm_scan.hip", "chunk_attn.hip", "attn_mfma.hip", "decode.hip", "proj_gemm.hip",
-           "abi.hip"]
+           "kvssm_scan_bwd.hip", "chunk_attn_bwd.hip", "abi.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed FP32 instructions are switched off for device code (the host pass of hipcc warns that

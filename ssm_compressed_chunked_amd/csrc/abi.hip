@@ -56,6 +56,39 @@ bool starts_chunk(int64_t pos, int64_t P, int64_t o) {
   return pos == 0 || (((pos - o) % P) + P) % P == 0;
 }
 
+// Checks shared by the scan and its backward (sizes, dtype and the forward inputs).
+int check_scan(const attamba_scan_args* a, const char* name) {
+  if (!dtype_ok(a->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "%s: dtype %d", name, a->dtype);
+  if (a->T < 0 || a->n_chunks < 0 || a->n_chunks > a->T || (a->T > 0 && a->n_chunks == 0))
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "%s: T=%d n_chunks=%d", name, a->T, a->n_chunks);
+  if (a->d <= 0 || a->d % 64 != 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "%s: d=%d not a positive multiple of 64", name, a->d);
+  if (a->N != 16 && a->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "%s: N=%d (16 or 32)", name, a->N);
+  if (static_cast<int64_t>(a->T) * a->d > INT32_MAX)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "%s: T*d exceeds 2^31 elements", name);
+  if (!a->chunk_cu || !a->x || !a->dt_k || !a->dt_v || !a->bm_k || !a->cm_k || !a->bm_v || !a->cm_v ||
+      !a->A_k || !a->A_v || !a->D_k || !a->D_v || !a->bias_k || !a->bias_v)
+    return fail(ATTAMBA_ERR_NULL_ARG, "%s: a required pointer is null", name);
+  return ATTAMBA_OK;
+}
+
+// Checks shared by the attention and its backward.
+int check_attn(const attamba_attn_args* a, const char* name) {
+  if (!dtype_ok(a->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "%s: dtype %d", name, a->dtype);
+  if (a->T < 0 || a->H < 1 || a->S < 1 || a->n_chunks < 0 || a->L < 0 ||
+      (a->T > 0 && (a->max_seqlen < 1 || a->n_chunks < 1)) ||
+      (a->mode != ATTAMBA_MASK_TRAIN && a->mode != ATTAMBA_MASK_TEST) || !(a->scale >= 0.0f))
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "%s: T=%d H=%d S=%d max_seqlen=%d n_chunks=%d L=%d mode=%d", name, a->T,
+                a->H, a->S, a->max_seqlen, a->n_chunks, a->L, a->mode);
+  if (a->hd != 32 && a->hd != 64 && a->hd != 128)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "%s: hd=%d (32, 64 or 128)", name, a->hd);
+  if (static_cast<int64_t>(a->T) * a->H * a->hd > INT32_MAX)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "%s: T*H*hd exceeds 2^31 elements", name);
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->kb || !a->vb || !a->seq_cu || !a->chunk_cu ||
+                   !a->token_chunk || !a->out))
+    return fail(ATTAMBA_ERR_NULL_ARG, "%s: a required pointer is null", name);
+  return ATTAMBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,16 +180,8 @@ int attamba_chunk_index(const int32_t* chunk_cu, int32_t n_chunks, int32_t T,
 
 int attamba_kvssm_scan(const attamba_scan_args* a, attamba_stream_t stream) {
   if (!a) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: args null");
-  if (!dtype_ok(a->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "kvssm_scan: dtype %d", a->dtype);
-  if (a->T < 0 || a->n_chunks < 0 || a->n_chunks > a->T || (a->T > 0 && a->n_chunks == 0))
-    return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan: T=%d n_chunks=%d", a->T, a->n_chunks);
-  if (a->d <= 0 || a->d % 64 != 0) return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan: d=%d not a positive multiple of 64", a->d);
-  if (a->N != 16 && a->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "kvssm_scan: N=%d (16 or 32)", a->N);
-  if (static_cast<int64_t>(a->T) * a->d > INT32_MAX)
-    return fail(ATTAMBA_ERR_UNSUPPORTED, "kvssm_scan: T*d exceeds 2^31 elements");
-  if (!a->chunk_cu || !a->x || !a->dt_k || !a->dt_v || !a->bm_k || !a->cm_k || !a->bm_v || !a->cm_v ||
-      !a->A_k || !a->A_v || !a->D_k || !a->D_v || !a->bias_k || !a->bias_v || !a->y_k || !a->y_v)
-    return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: a required pointer is null");
+  if (const int st = check_scan(a, "kvssm_scan")) return st;
+  if (!a->y_k || !a->y_v) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: y_k or y_v null");
   if (!a->kb != !a->vb) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: kb and vb must both be set or both null");
   if (!a->h_last_k != !a->h_last_v) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: h_last_k/h_last_v must match");
   if (a->h_last_k && (!a->seq_cu || a->S < 1))
@@ -164,24 +189,58 @@ int attamba_kvssm_scan(const attamba_scan_args* a, attamba_stream_t stream) {
   return hip_status(attamba::launch_kvssm_scan(*a, reinterpret_cast<hipStream_t>(stream)), "kvssm_scan launch");
 }
 
+int attamba_kvssm_scan_bwd(const attamba_scan_bwd_args* b, attamba_stream_t stream) {
+  if (!b) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan_bwd: args null");
+  const attamba_scan_args* a = &b->fwd;
+  if (const int st = check_scan(a, "kvssm_scan_bwd")) return st;
+  if (!b->gy_k || !b->gy_v || !b->dx_k || !b->dx_v || !b->ddt_k || !b->ddt_v || !b->dbm_k || !b->dcm_k ||
+      !b->dbm_v || !b->dcm_v || !b->dA_k || !b->dA_v || !b->dD_k || !b->dD_v || !b->dbias_k || !b->dbias_v)
+    return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan_bwd: a required gradient pointer is null");
+  if (!b->gkb != !b->gvb) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan_bwd: gkb and gvb must both be set or both null");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  attamba::ZeroList z{};
+  float* bufs[attamba::kMaxZero] = {b->dbm_k, b->dcm_k, b->dbm_v, b->dcm_v, b->dA_k, b->dA_v,
+                                    b->dD_k, b->dD_v, b->dbias_k, b->dbias_v};
+  const int counts[attamba::kMaxZero] = {a->T * a->N, a->T * a->N, a->T * a->N, a->T * a->N, a->d * a->N,
+                                         a->d * a->N, a->d, a->d, a->d, a->d};
+  for (int i = 0; i < attamba::kMaxZero; ++i) { z.ptr[i] = bufs[i]; z.count[i] = counts[i]; }
+  if (const int st = hip_status(attamba::launch_zero(z, attamba::kMaxZero, s), "kvssm_scan_bwd zero")) return st;
+  attamba::ScanBwdParams p{};
+  p.T = a->T; p.d = a->d; p.n_chunks = a->n_chunks; p.chunk_cu = a->chunk_cu;
+  const bool sep = a->x_v && a->x_v != a->x;
+  p.side[0] = {a->x, a->dt_k, a->bm_k, a->cm_k, b->gy_k, b->gkb, a->A_k, a->D_k, a->bias_k,
+               b->dx_k, b->ddt_k, b->dbm_k, b->dcm_k, b->dA_k, b->dD_k, b->dbias_k};
+  p.side[1] = {sep ? a->x_v : a->x, a->dt_v, a->bm_v, a->cm_v, b->gy_v, b->gvb, a->A_v, a->D_v, a->bias_v,
+               b->dx_v, b->ddt_v, b->dbm_v, b->dcm_v, b->dA_v, b->dD_v, b->dbias_v};
+  return hip_status(attamba::launch_kvssm_scan_bwd(p, a->N, a->dtype, s), "kvssm_scan_bwd launch");
+}
+
 int attamba_chunk_attn_fwd(const attamba_attn_args* a, attamba_stream_t stream) {
   if (!a) return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_fwd: args null");
-  if (!dtype_ok(a->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "chunk_attn_fwd: dtype %d", a->dtype);
-  if (a->T < 0 || a->H < 1 || a->S < 1 || a->n_chunks < 0 || a->L < 0 ||
-      (a->T > 0 && (a->max_seqlen < 1 || a->n_chunks < 1)) ||
-      (a->mode != ATTAMBA_MASK_TRAIN && a->mode != ATTAMBA_MASK_TEST) || !(a->scale >= 0.0f))
-    return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_attn_fwd: T=%d H=%d S=%d max_seqlen=%d n_chunks=%d L=%d mode=%d", a->T,
-                a->H, a->S, a->max_seqlen, a->n_chunks, a->L, a->mode);
-  if (a->hd != 32 && a->hd != 64 && a->hd != 128)
-    return fail(ATTAMBA_ERR_UNSUPPORTED, "chunk_attn_fwd: hd=%d (32, 64 or 128)", a->hd);
-  if (static_cast<int64_t>(a->T) * a->H * a->hd > INT32_MAX)
-    return fail(ATTAMBA_ERR_UNSUPPORTED, "chunk_attn_fwd: T*H*hd exceeds 2^31 elements");
-  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->kb || !a->vb || !a->seq_cu || !a->chunk_cu ||
-                   !a->token_chunk || !a->out))
-    return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_fwd: a required pointer is null");
+  if (const int st = check_attn(a, "chunk_attn_fwd")) return st;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / std::sqrt(static_cast<float>(a->hd));
   return hip_status(attamba::launch_chunk_attn(*a, scale, reinterpret_cast<hipStream_t>(stream)),
                     "chunk_attn_fwd launch");
+}
+
+int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* b, attamba_stream_t stream) {
+  if (!b) return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_bwd: args null");
+  const attamba_attn_args* a = &b->fwd;
+  if (const int st = check_attn(a, "chunk_attn_bwd")) return st;
+  if (a->T > 0 && (!a->lse || !b->dout || !b->dq || !b->dk || !b->dv || !b->dkb || !b->dvb || !b->workspace))
+    return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_bwd: lse, dout, a gradient or the workspace is null");
+  attamba::AttnBwdParams p{};
+  attamba::AttnParams& f = p.f;
+  f.T = a->T; f.H = a->H; f.S = a->S; f.max_seqlen = a->max_seqlen; f.L = a->L;
+  f.train = a->mode == ATTAMBA_MASK_TRAIN ? 1 : 0;
+  f.scale = a->scale > 0.0f ? a->scale : 1.0f / std::sqrt(static_cast<float>(a->hd));
+  f.q = a->q; f.k = a->k; f.v = a->v; f.kb = a->kb; f.vb = a->vb;
+  f.seq_cu = a->seq_cu; f.chunk_cu = a->chunk_cu; f.token_chunk = a->token_chunk;
+  f.out = a->out; f.lse = a->lse;
+  p.dout = b->dout; p.dq = b->dq; p.dk = b->dk; p.dv = b->dv; p.dkb = b->dkb; p.dvb = b->dvb;
+  p.delta = b->workspace; p.n_chunks = a->n_chunks;
+  return hip_status(attamba::launch_chunk_attn_bwd(p, a->hd, a->dtype, reinterpret_cast<hipStream_t>(stream)),
+                    "chunk_attn_bwd launch");
 }
 
 int attamba_input_proj(const attamba_proj_args* a, attamba_stream_t stream) {

@@ -3,36 +3,13 @@
 // M_test (Eq. 7) and the window of L leading tokens (Eq. 8); causal reading of M_test from
 // the Referee Report's second major comment).
 //
-// Every query row i sees two contiguous key ranges, so no mask is materialised:
-//   boundary phase: compact boundary states kb/vb of the chunks c0 .. c0 + E_i - 1 of its
-//                   sequence (the chunks that end before w_i);
-//   band phase:     per-token keys k/v at positions w_i .. i,
-// with w_i = max(s0, i - L + 1) (i + 1 when L = 0) and, under M_train, w_i = min(w_i, start of
-// i's chunk). Both ranges grow monotonically with i, which the tiled kernel exploits.
+// Every query row sees two contiguous key ranges (attn_geom.h), so no mask is materialised:
+// a boundary phase over compact boundary states kb/vb and a band phase over per-token keys.
 #include "common.h"
-#include "kernels.h"
+#include "attn_geom.h"
 
 namespace attamba {
 namespace {
-
-// Row geometry shared by the kernels.
-struct RowInfo {
-  int w;   // first band position
-  int E;   // boundary states visible (chunks c0 .. c0 + E - 1)
-};
-
-__device__ __forceinline__ RowInfo row_info(const AttnParams& p, int i, int s0, int s1, int c0) {
-  RowInfo r;
-  int w = i - p.L + 1;
-  if (w < s0) w = s0;
-  if (p.train) {
-    const int cs = p.chunk_cu[p.token_chunk[i]];
-    if (cs < w) w = cs;
-  }
-  r.w = w;
-  r.E = (w < s1) ? p.token_chunk[w] - c0 : p.token_chunk[s1 - 1] + 1 - c0;
-  return r;
-}
 
 // Generic kernel: one lane per query row, keys visited one at a time with an online softmax in
 // float32. Used for float32 activations and for head dims without an MFMA kernel.
@@ -45,7 +22,7 @@ __global__ __launch_bounds__(64) void attn_rowwise_kernel(AttnParams p) {
   const int i = r0 + threadIdx.x;
   if (i >= s1) return;
   const int c0 = p.token_chunk[s0];
-  const RowInfo ri = row_info(p, i, s0, s1, c0);
+  const RowGeom ri = row_geom(p, i, s0, s1, c0);
   const size_t rs = static_cast<size_t>(p.H) * HD;   // row stride of [., H, HD] tensors
   const T* q = static_cast<const T*>(p.q) + i * rs + h * HD;
   float qs[HD], acc[HD];

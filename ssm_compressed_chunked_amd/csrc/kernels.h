@@ -49,6 +49,41 @@ struct ProjParams {
 };
 hipError_t launch_proj_gemm(const ProjParams& p, hipStream_t stream);
 
+// Backward of the KV-SSM scan: one side per SSM (index 0 = SSM_K, 1 = SSM_V).
+struct ScanBwdSide {
+  const void *x, *dt, *bm, *cm;   // forward inputs of this SSM
+  const void *gy, *gb;            // gradients of its per-token outputs [T, d] and boundary
+                                  // states [n_chunks, d] (gb may be null)
+  const float *A, *D, *bias;
+  void *dx, *ddt;                 // [T, d] activation dtype
+  float *dbm, *dcm;               // [T, N], accumulated (zeroed first)
+  float *dA, *dD, *dbias;         // [d, N], [d], [d], accumulated (zeroed first)
+};
+struct ScanBwdParams {
+  int T, d, n_chunks;
+  const int32_t* chunk_cu;
+  ScanBwdSide side[2];
+};
+hipError_t launch_kvssm_scan_bwd(const ScanBwdParams& p, int N, int dtype, hipStream_t stream);
+
+// Zero-fill of up to kMaxZero float buffers in one launch.
+constexpr int kMaxZero = 10;
+struct ZeroList {
+  float* ptr[kMaxZero];
+  int count[kMaxZero];
+};
+hipError_t launch_zero(const ZeroList& z, int n, hipStream_t stream);
+
+// Backward of the chunk attention.
+struct AttnBwdParams {
+  AttnParams f;                   // forward geometry and inputs; f.out and f.lse are read
+  const void* dout;
+  void *dq, *dk, *dv, *dkb, *dvb;
+  float* delta;                   // [H, T] rowsum(dout * out)
+  int n_chunks;
+};
+hipError_t launch_chunk_attn_bwd(const AttnBwdParams& p, int hd, int dtype, hipStream_t stream);
+
 int decode_max_splits(int cap, int L);
 size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L);
 hipError_t launch_decode_step(const attamba_decode_cache& c, const attamba_decode_inputs& in,

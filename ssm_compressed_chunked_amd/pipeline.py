@@ -58,7 +58,34 @@ def prefill_forward(act: dict, params: dict, seq_cu_host, H: int, hd: int, P: in
                                 scan["vb"].view(n, H, hd), seq_cu, layout.chunk_cu,
                                 layout.token_chunk, max(max_len, 1), L, mode,
                                 return_lse=want_lse, stream=stream)
-    return dict(layout=layout, scan=scan, out=out, lse=lse, seq_cu=seq_cu)
+    return dict(layout=layout, scan=scan, out=out, lse=lse, seq_cu=seq_cu, max_len=max(max_len, 1))
+
+
+def prefill_backward(res: dict, act: dict, params: dict, dout: torch.Tensor, H: int, hd: int,
+                     L: int, mode: int, stream=None) -> dict:
+    """Backward of `prefill_forward` for the output gradient dout [T, H, hd]: the attention
+    backward (gradients of q, of the per-token keys/values and of the boundary states), then
+    the KV-SSM backward with the boundary gradients added at each chunk's last token. res is
+    prefill_forward's result (its out and lse are required). Returns the attention gradients
+    (dq, dk, dv, dkb, dvb) and the scan gradients (dx_k, dx_v, ddt_k, ddt_v, dbm_*, dcm_*,
+    dA_*, dD_*, dbias_*); when both SSMs read x, x's gradient through them is dx_k + dx_v."""
+    x = act["x"]
+    T, d = x.shape
+    lay = res["layout"]
+    n = lay.n_chunks
+    scan = res["scan"]
+    max_len = res["max_len"]
+    ga = B.chunk_attn_bwd(act["q"].view(T, H, hd), scan["y_k"].view(T, H, hd),
+                          scan["y_v"].view(T, H, hd), scan["kb"].view(n, H, hd),
+                          scan["vb"].view(n, H, hd), res["seq_cu"], lay.chunk_cu,
+                          lay.token_chunk, max_len, L, mode, res["out"], res["lse"], dout,
+                          stream=stream)
+    gs = B.kvssm_scan_bwd(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"],
+                          act["bm_v"], act["cm_v"], params["A_k"], params["A_v"], params["D_k"],
+                          params["D_v"], params["bias_k"], params["bias_v"], lay.chunk_cu,
+                          ga["dk"].view(T, d), ga["dv"].view(T, d), gkb=ga["dkb"].view(n, d),
+                          gvb=ga["dvb"].view(n, d), x_v=act.get("x_v"), stream=stream)
+    return {**ga, **gs}
 
 
 PROJ_NAMES = ("q", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v")

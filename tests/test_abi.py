@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_and_exports_agree():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert set(names) == set(B.EXPORTS), (set(names) ^ set(B.EXPORTS))
     lib = att.lib()
     for n in names:
@@ -127,3 +127,40 @@ def test_input_proj_validates_before_launch():
     assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_NULL_ARG       # x, w, out null
     a.T = 1 << 24
     assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_UNSUPPORTED    # T*d >= 2^31
+
+
+def test_backward_entry_points_validate_before_launch():
+    lib = att.lib()
+    assert lib.attamba_chunk_attn_bwd(None, None) == B.ERR_NULL_ARG
+    assert lib.attamba_kvssm_scan_bwd(None, None) == B.ERR_NULL_ARG
+    fake = C.c_void_p(0x1000)          # never dereferenced: validation fails before any launch
+    b = B.AttnBwdArgs()
+    f = b.fwd
+    f.T, f.H, f.hd, f.dtype, f.S, f.max_seqlen, f.n_chunks, f.L, f.mode = 64, 2, 64, 1, 1, 64, 8, 0, 0
+    for name in ("q", "k", "v", "kb", "vb", "seq_cu", "chunk_cu", "token_chunk", "out"):
+        setattr(f, name, fake)
+    assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_NULL_ARG   # lse, dout, grads
+    f.hd = 48
+    assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_UNSUPPORTED
+    f.hd, f.mode = 64, 7
+    assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_BAD_SHAPE
+    f.mode, f.dtype = 0, 9
+    assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_BAD_DTYPE
+
+    s = B.ScanBwdArgs()
+    a = s.fwd
+    a.T, a.d, a.N, a.dtype, a.n_chunks = 64, 128, 16, 1, 8
+    for name in ("chunk_cu", "x", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v", "A_k", "A_v",
+                 "D_k", "D_v", "bias_k", "bias_v"):
+        setattr(a, name, fake)
+    assert lib.attamba_kvssm_scan_bwd(C.byref(s), None) == B.ERR_NULL_ARG   # gradients null
+    a.N = 8
+    assert lib.attamba_kvssm_scan_bwd(C.byref(s), None) == B.ERR_UNSUPPORTED
+    a.N, a.d = 16, 96
+    assert lib.attamba_kvssm_scan_bwd(C.byref(s), None) == B.ERR_BAD_SHAPE
+    a.d = 128
+    for name in ("gy_k", "gy_v", "dx_k", "dx_v", "ddt_k", "ddt_v", "dbm_k", "dcm_k", "dbm_v",
+                 "dcm_v", "dA_k", "dA_v", "dD_k", "dD_v", "dbias_k", "dbias_v"):
+        setattr(s, name, fake)
+    s.gkb = fake
+    assert lib.attamba_kvssm_scan_bwd(C.byref(s), None) == B.ERR_NULL_ARG   # gkb without gvb

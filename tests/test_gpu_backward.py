@@ -1,0 +1,293 @@
+"""GPU parity of the backward pass (attamba_chunk_attn_bwd, attamba_kvssm_scan_bwd) against the
+CPU oracle's reverse-mode gradients on the same seeded inputs and output gradients.
+
+Bars: the forward's relative bars (float32 1e-4, bf16 2e-2); gradients have no fixed scale, so
+the absolute part of each bar (1e-5, 2e-2) is taken relative to s = min(1, max |ref|) of that
+output, which never exceeds the forward's bar. The float32 sums over channels or tokens (dBm,
+dCm, dA, dD, dbias) are accumulated in another order, with atomics; their bar adds 1e-5 of the
+output's largest magnitude for the float32 rounding of long sums. Those outputs are float32 even
+for bf16 activations: where both sides get the same inputs (the standalone scan test) they are
+held to the float32 bar. In the bf16 forward + backward chain they sum thousands of terms that
+carry the bf16 rounding of the attention gradients (relative 2^-9 each, random in sign), so an
+element whose terms cancel has a large relative error; there the 2e-2 bar is normwise: 2e-2 of
+the output's largest magnitude.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssm_compressed_chunked_amd as att
+from ssm_compressed_chunked_amd.pipeline import chunk_layout, prefill_backward, prefill_forward
+from workloads import (PREFILL_BF16, TINY_FP32, TRAIN_BF16, VARCHUNK_BF16, make_output_grad,
+                       make_prefill, make_ragged_prefill)
+
+pytestmark = pytest.mark.gpu
+
+MODE = {"train": att.MASK_TRAIN, "test": att.MASK_TEST}
+SUMS = ("dbm", "dcm", "dA", "dD", "dbias")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_close(got, ref, dtype, what, sum_output=False):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    top = float(np.abs(ref).max()) if ref.size else 0.0
+    sc = min(1.0, top)
+    if dtype == "fp32":
+        bound = 1e-4 * np.abs(ref) + 1e-5 * sc
+    else:
+        bound = 2e-2 * np.abs(ref) + 2e-2 * sc
+    if sum_output:
+        bound = bound + (1e-5 if dtype == "fp32" else 2e-2) * top
+    err = np.abs(got - ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; max err "
+                           f"{err.max():.3e} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+    return float(err.max())
+
+
+def _inputs(base, over, lens, rnd, seed=21):
+    cfg = base.with_(**over)
+    if lens is None:
+        c = cfg.with_(chunking="random") if rnd else cfg
+        return cfg, make_prefill(c, seed=seed)
+    chunk_lens = None
+    if rnd:
+        from workloads import draw_chunk_lengths
+        crng = np.random.default_rng(seed)
+        chunk_lens = []
+        for n in lens:
+            chunk_lens += draw_chunk_lengths(crng, n, cfg.chunk_len_lo, cfg.chunk_len_hi)
+    inp = make_ragged_prefill(cfg, lens, seed=seed, chunk_lens=chunk_lens)
+    return inp.cfg, inp
+
+
+def _layout(inp, cfg, rnd):
+    T = int(inp.seq_cu[-1])
+    P = None if rnd else cfg.P
+    seq_cu = torch.from_numpy(inp.seq_cu).cuda()
+    lay = chunk_layout(inp.seq_cu, seq_cu, T, P, cfg.layer_idx, chunk_lens=inp.chunk_lens)
+    ref = oracle.segment(inp.seq_cu, P, cfg.layer_idx, inp.chunk_lens)
+    np.testing.assert_array_equal(lay.chunk_cu.cpu().numpy(), ref[0])
+    return seq_cu, lay, ref
+
+
+def _scatter_ends(per_token, per_chunk, chunk_cu):
+    """Total gradient of the per-token outputs: the boundary-state gradient of each chunk added
+    at its last token."""
+    tot = np.array(per_token, dtype=np.float64)
+    ends = np.asarray(chunk_cu[1:], dtype=np.int64) - 1
+    tot[ends] += per_chunk
+    return tot
+
+
+# ------------------------------------------------------------------------- scan backward
+SCAN_CASES = [
+    # (name, base, overrides, lengths, random chunks, separate SSM_V input, boundary grads)
+    ("fp32_tiny", TINY_FP32, {}, None, False, False, True),
+    ("bf16_o3_ragged", TRAIN_BF16, dict(d=128, H=2, P=8, layer_idx=3), [70, 1, 130, 9], False, False, True),
+    ("bf16_N32_P5", PREFILL_BF16, dict(d=128, H=2, N=32, P=5, layer_idx=2), [90, 41], False, False, True),
+    ("bf16_random_chunks", VARCHUNK_BF16, dict(d=128, H=2), [150, 77], True, False, True),
+    ("bf16_P64_long_chunks", PREFILL_BF16, dict(d=128, H=2, P=64, layer_idx=9), [200, 64], False, False, True),
+    ("bf16_separate_v_input", TRAIN_BF16, dict(d=192, H=3, P=4), [60, 35], False, True, True),
+    ("fp32_no_boundary_grads", TINY_FP32, dict(d=128, H=2, P=3, layer_idx=1), [50, 17], False, False, False),
+    ("bf16_P1", PREFILL_BF16, dict(d=64, H=1, P=1), [40], False, False, True),
+]
+
+
+@pytest.mark.parametrize("name,base,over,lens,rnd,sepv,use_gb", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_scan_backward_elementwise(name, base, over, lens, rnd, sepv, use_gb):
+    cfg, inp = _inputs(base, over, lens, rnd)
+    T, d, N = int(inp.seq_cu[-1]), cfg.d, cfg.N
+    say(f"scan backward {name}: T={T} d={d} N={N} P={cfg.P} random={rnd} sepv={sepv}")
+    _, lay, ref_lay = _layout(inp, cfg, rnd)
+    n = lay.n_chunks
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    par = {k: v.cuda() for k, v in inp.param.items()}
+    x_v = make_output_grad((T, d), cfg.dtype, seed=5).cuda() if sepv else None
+    gy = {t: make_output_grad((T, d), cfg.dtype, seed=10 + i) for i, t in enumerate("kv")}
+    gb = {t: make_output_grad((n, d), cfg.dtype, seed=20 + i) for i, t in enumerate("kv")} if use_gb else None
+    g = att.kvssm_scan_bwd(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"], act["bm_v"],
+                           act["cm_v"], par["A_k"], par["A_v"], par["D_k"], par["D_v"], par["bias_k"],
+                           par["bias_v"], lay.chunk_cu, gy["k"].cuda(), gy["v"].cuda(),
+                           gkb=gb["k"].cuda() if gb else None, gvb=gb["v"].cuda() if gb else None,
+                           x_v=x_v)
+    torch.cuda.synchronize()
+    for t in "kv":
+        xin = (x_v.cpu() if (sepv and t == "v") else inp.act["x"]).to(torch.float64).numpy()
+        gyt = gy[t].to(torch.float64).numpy()
+        if gb:
+            gyt = _scatter_ends(gyt, gb[t].to(torch.float64).numpy(), ref_lay[0])
+        ref = oracle.selective_scan_backward(xin, inp.f64(f"dt_{t}"), inp.f64(f"bias_{t}"),
+                                             inp.f64(f"A_{t}"), inp.f64(f"bm_{t}"), inp.f64(f"cm_{t}"),
+                                             inp.f64(f"D_{t}"), ref_lay[0], gyt)
+        for key, mine in (("dx", f"dx_{t}"), ("ddt", f"ddt_{t}"), ("dBm", f"dbm_{t}"),
+                          ("dCm", f"dcm_{t}"), ("dA", f"dA_{t}"), ("dD", f"dD_{t}"),
+                          ("dbias", f"dbias_{t}")):
+            is_sum = key not in ("dx", "ddt")
+            err = check_close(g[mine].float().cpu().numpy(), ref[key], "fp32" if is_sum else cfg.dtype,
+                              f"{name} {mine}", sum_output=is_sum)
+            say(f"  {mine}: max err {err:.2e}")
+
+
+# -------------------------------------------------------------------- attention backward
+ATTN_CASES = [
+    # (name, base, overrides, lengths, random chunks)
+    ("fp32_tiny_train", TINY_FP32, {}, None, False),
+    ("fp32_hd64_test_L7", TINY_FP32, dict(d=128, H=2, hd=64, P=3, L=7, mode="test", layer_idx=1), [90, 33], False),
+    ("bf16_train_L64_o3", TRAIN_BF16, dict(d=128, H=2), [300, 129], False),
+    ("bf16_test_L0_empty_rows", PREFILL_BF16, dict(d=128, H=2, L=0, P=4), [70, 1, 0, 45], False),
+    ("bf16_test_L64", PREFILL_BF16, dict(d=128, H=2), [333], False),
+    ("bf16_P1_test_L0", PREFILL_BF16, dict(d=128, H=2, P=1, L=0), [150], False),
+    ("bf16_train_L0_P4", PREFILL_BF16, dict(d=128, H=2, P=4, L=0, mode="train"), [257], False),
+    ("bf16_random_chunks", VARCHUNK_BF16, dict(d=128, H=2), [150, 211], True),
+    ("bf16_hd128_train_L200", TRAIN_BF16, dict(d=256, H=2, hd=128, L=200), [520], False),
+    ("bf16_hd32_test_L5", PREFILL_BF16, dict(d=128, H=4, hd=32, L=5, P=3, layer_idx=1), [99, 2], False),
+    ("bf16_P128_train_L16", TRAIN_BF16, dict(d=128, H=2, P=128, L=16, layer_idx=5), [700], False),
+]
+
+
+@pytest.mark.parametrize("name,base,over,lens,rnd", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_backward_elementwise(name, base, over, lens, rnd):
+    """q, k, v are seeded directly (kb, vb = k, v at the chunk ends, as the scan makes them)."""
+    cfg, inp = _inputs(base, over, lens, rnd)
+    T, H, hd = int(inp.seq_cu[-1]), cfg.H, cfg.hd
+    say(f"attention backward {name}: T={T} H={H} hd={hd} P={cfg.P} L={cfg.L} mode={cfg.mode}")
+    seq_cu, lay, ref_lay = _layout(inp, cfg, rnd)
+    n = lay.n_chunks
+    q = make_output_grad((T, H, hd), cfg.dtype, seed=31)
+    k = make_output_grad((T, H, hd), cfg.dtype, seed=32)
+    v = make_output_grad((T, H, hd), cfg.dtype, seed=33)
+    dout = make_output_grad((T, H, hd), cfg.dtype, seed=34)
+    ends = torch.from_numpy(np.asarray(ref_lay[0][1:], dtype=np.int64) - 1)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    kb, vb = kd[ends.cuda()].contiguous(), vd[ends.cuda()].contiguous()
+    max_len = max(int(np.diff(inp.seq_cu).max()), 1)
+    out, lse = att.chunk_attn_fwd(qd, kd, vd, kb, vb, seq_cu, lay.chunk_cu, lay.token_chunk, max_len,
+                                  cfg.L, MODE[cfg.mode])
+    g = att.chunk_attn_bwd(qd, kd, vd, kb, vb, seq_cu, lay.chunk_cu, lay.token_chunk, max_len, cfg.L,
+                           MODE[cfg.mode], out, lse, dout.cuda())
+    torch.cuda.synchronize()
+    f = lambda t: t.to(torch.float64).numpy()
+    dq, dk, dv = oracle.chunk_attention_backward(f(q), f(k), f(v), inp.seq_cu, ref_lay[1], ref_lay[2],
+                                                 cfg.L, cfg.mode, f(dout))
+    check_close(g["dq"].float().cpu().numpy(), dq, cfg.dtype, "dq")
+    dk_tot = _scatter_ends(g["dk"].float().cpu().numpy(), g["dkb"].float().cpu().numpy(), ref_lay[0])
+    dv_tot = _scatter_ends(g["dv"].float().cpu().numpy(), g["dvb"].float().cpu().numpy(), ref_lay[0])
+    check_close(dk_tot, dk, cfg.dtype, "dk (per-token + boundary)")
+    check_close(dv_tot, dv, cfg.dtype, "dv (per-token + boundary)")
+
+
+# --------------------------------------------------------------- forward + backward chain
+def _oracle_chain(inp, cfg, P, dout64, seqs):
+    """Oracle forward and backward over the sequences `seqs` (each is independent)."""
+    f = {k: inp.f64(k) for k in list(inp.act) + list(inp.param)}
+    H, hd, d = cfg.H, cfg.hd, cfg.d
+    out = {}
+    for s in seqs:
+        a, b = int(inp.seq_cu[s]), int(inp.seq_cu[s + 1])
+        if b <= a:
+            continue
+        sub = {k: (v[a:b] if v.ndim == 2 and v.shape[0] == int(inp.seq_cu[-1]) else v) for k, v in f.items()}
+        lens = None
+        if inp.chunk_lens is not None:
+            cu_all = oracle.segment(inp.seq_cu, None, 0, inp.chunk_lens)[0]
+            cu = cu_all[(cu_all >= a) & (cu_all <= b)] - a
+            lens = np.diff(cu)
+        seq_cu = np.array([0, b - a], dtype=np.int32)
+        ref = oracle.kvssm_forward(sub, seq_cu, H, hd, P, cfg.layer_idx, cfg.L, cfg.mode,
+                                   chunk_lens=lens)
+        n = b - a
+        cu, tc, ie = oracle.segment(seq_cu, P, cfg.layer_idx, lens)
+        dq, dk, dv = oracle.chunk_attention_backward(sub["q"].reshape(n, H, hd), ref["y_k"].reshape(n, H, hd),
+                                                     ref["y_v"].reshape(n, H, hd), seq_cu, tc, ie, cfg.L,
+                                                     cfg.mode, dout64[a:b])
+        res = dict(dq=dq)
+        for t, gy in (("k", dk), ("v", dv)):
+            g = oracle.selective_scan_backward(sub["x"], sub[f"dt_{t}"], sub[f"bias_{t}"], sub[f"A_{t}"],
+                                               sub[f"bm_{t}"], sub[f"cm_{t}"], sub[f"D_{t}"], cu,
+                                               gy.reshape(n, d))
+            for key, val in g.items():
+                res[f"{key}_{t}"] = val
+        out[s] = res
+    return out
+
+
+CHAIN_CASES = [
+    ("fp32_tiny", TINY_FP32, {}, None, False),
+    ("bf16_train_L64_o3", TRAIN_BF16, dict(d=128, H=2), [200, 75], False),
+    ("bf16_random_chunks", VARCHUNK_BF16, dict(d=128, H=2), [120], True),
+]
+
+
+@pytest.mark.parametrize("name,base,over,lens,rnd", CHAIN_CASES, ids=[c[0] for c in CHAIN_CASES])
+def test_forward_backward_chain(name, base, over, lens, rnd):
+    cfg, inp = _inputs(base, over, lens, rnd)
+    T = int(inp.seq_cu[-1])
+    say(f"chain {name}: T={T} d={cfg.d} P={cfg.P} L={cfg.L} mode={cfg.mode}")
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    par = {k: v.cuda() for k, v in inp.param.items()}
+    P = None if rnd else cfg.P
+    dout = make_output_grad((T, cfg.H, cfg.hd), cfg.dtype, seed=41)
+    res = prefill_forward(act, par, inp.seq_cu, cfg.H, cfg.hd, P, cfg.layer_idx, cfg.L, MODE[cfg.mode],
+                          chunk_lens=inp.chunk_lens)
+    g = prefill_backward(res, act, par, dout.cuda(), cfg.H, cfg.hd, cfg.L, MODE[cfg.mode])
+    torch.cuda.synchronize()
+    S = len(inp.seq_cu) - 1
+    ref = _oracle_chain(inp, cfg, P, dout.to(torch.float64).numpy(), range(S))
+    _compare_chain(g, ref, inp, cfg, list(ref))
+
+
+def _compare_chain(g, ref, inp, cfg, seqs):
+    sums = {}
+    for s in seqs:
+        a, b = int(inp.seq_cu[s]), int(inp.seq_cu[s + 1])
+        r = ref[s]
+        check_close(g["dq"][a:b].float().cpu().numpy(), r["dq"], cfg.dtype, f"dq seq {s}")
+        for t in "kv":
+            for key, mine in (("dx", f"dx_{t}"), ("ddt", f"ddt_{t}"), ("dBm", f"dbm_{t}"), ("dCm", f"dcm_{t}")):
+                check_close(g[mine][a:b].float().cpu().numpy(), r[f"{key}_{t}"], cfg.dtype, f"{mine} seq {s}",
+                            sum_output=key in ("dBm", "dCm"))
+            for key in ("dA", "dD", "dbias"):
+                sums[f"{key}_{t}"] = sums.get(f"{key}_{t}", 0) + r[f"{key}_{t}"]
+    for t in "kv":
+        for key, mine in (("dA", f"dA_{t}"), ("dD", f"dD_{t}"), ("dbias", f"dbias_{t}")):
+            check_close(g[mine].float().cpu().numpy(), sums[f"{key}_{t}"], cfg.dtype, mine, sum_output=True)
+
+
+def test_full_size_train_chain_sampled():
+    """The M_train workload at full size (B=4, n=2048, d=1024, 16 heads x 64, P=8, L=64, layer 3),
+    in the launch configuration the benchmark times. The output gradient is nonzero on the first
+    and last sequence only, so the oracle runs on those two and every parameter-gradient sum is
+    still checked in full; the gradients of the other sequences must be exactly zero."""
+    cfg = TRAIN_BF16
+    say(f"full-size chain {cfg.name}")
+    inp = make_prefill(cfg)
+    T = cfg.T
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    par = {k: v.cuda() for k, v in inp.param.items()}
+    dout = make_output_grad((T, cfg.H, cfg.hd), cfg.dtype, seed=42)
+    S = len(inp.seq_cu) - 1
+    keep = [0, S - 1]
+    mask = torch.zeros(T, dtype=torch.bool)
+    for s in keep:
+        mask[int(inp.seq_cu[s]):int(inp.seq_cu[s + 1])] = True
+    dout[~mask] = 0
+    res = prefill_forward(act, par, inp.seq_cu, cfg.H, cfg.hd, cfg.P, cfg.layer_idx, cfg.L, MODE[cfg.mode])
+    g = prefill_backward(res, act, par, dout.cuda(), cfg.H, cfg.hd, cfg.L, MODE[cfg.mode])
+    torch.cuda.synchronize()
+    say("  GPU done; oracle on two sequences")
+    ref = _oracle_chain(inp, cfg, cfg.P, dout.to(torch.float64).numpy(), keep)
+    _compare_chain(g, ref, inp, cfg, keep)
+    for s in range(1, S - 1):
+        a, b = int(inp.seq_cu[s]), int(inp.seq_cu[s + 1])
+        for key in ("dq", "dx_k", "dx_v", "ddt_k", "ddt_v", "dbm_k", "dcm_v"):
+            assert not g[key][a:b].any(), (key, s)

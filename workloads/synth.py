@@ -136,6 +136,14 @@ def make_projection(T: int, d: int, N: int, seed: int) -> ProjInputs:
                       w=torch.from_numpy(w).to(torch.bfloat16), widths=widths)
 
 
+def make_output_grad(shape, dtype: str, seed: int) -> torch.Tensor:
+    """A seeded upstream gradient (of an attention output, an SSM output or a boundary state):
+    N(0, 1), rounded to the storage type."""
+    rng = np.random.default_rng((seed, 3))
+    g = rng.standard_normal(tuple(shape), dtype=np.float32)
+    return torch.from_numpy(g).to(torch_dtype(dtype))
+
+
 @dataclass
 class DecodeInputs:
     """Synthetic decode workload: a cache of `n_bound` boundary states and an L-slot window
