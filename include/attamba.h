@@ -309,7 +309,7 @@ typedef struct {
   void* dv;            /* [T, H, hd] out: gradient of v */
   void* dkb;           /* [n_chunks, H, hd] out: gradient of kb */
   void* dvb;           /* [n_chunks, H, hd] out: gradient of vb */
-  float* workspace;    /* [H, T] device scratch, float32 */
+  float* workspace;    /* device scratch of (H + 2) * T 4-byte elements */
 } attamba_attn_bwd_args;
 
 int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* args, attamba_stream_t stream);
@@ -321,7 +321,9 @@ int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* args, attamba_stream_t s
  *          when both SSMs read x, the gradient of x is dx_k + dx_v;
  *   ddt_S  gradient of the step-size pre-activation dt_S;
  *   dbm_S, dcm_S [T, N], dA_S [d, N], dD_S, dbias_S [d]: float32, summed over channels / tokens.
- * Errors: as attamba_kvssm_scan, plus NULL_ARG for a missing gradient pointer. */
+ * bm_k, cm_k, bm_v, cm_v must be 16-byte aligned (each lane reads half a row as vectors).
+ * Errors: as attamba_kvssm_scan, plus NULL_ARG for a missing gradient pointer and BAD_SHAPE
+ * for a misaligned bm/cm pointer. */
 typedef struct {
   attamba_scan_args fwd;
   const void* gy_k;    /* [T, d] gradient of y_k */

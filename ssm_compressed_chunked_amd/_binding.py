@@ -382,8 +382,8 @@ def chunk_attn_bwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: i
     b.fwd.lse = _dev(lse, "lse", torch.float32, H * T)
     b.dout = _dev(dout, "dout", act, T * H * hd)
     if workspace is None:
-        workspace = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    b.workspace = _dev(workspace, "workspace", torch.float32, H * T)
+        workspace = torch.empty((H + 2, T), dtype=torch.float32, device=q.device)
+    b.workspace = _dev(workspace, "workspace", torch.float32, (H + 2) * T)
     g = dict(dq=torch.empty_like(q), dk=torch.empty_like(q), dv=torch.empty_like(q),
              dkb=torch.empty((n_chunks, H, hd), dtype=act, device=q.device),
              dvb=torch.empty((n_chunks, H, hd), dtype=act, device=q.device))

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattamba.so")
 SOURCES = ["boundaries.hip", "kvssm_scan.hip", "chunk_attn.hip", "attn_mfma.hip", "decode.hip", "proj_gemm.hip",
-           "kvssm_scan_bwd.hip", "chunk_attn_bwd.hip", "abi.hip"]
+           "kvssm_scan_bwd.hip", "chunk_attn_bwd.hip", "attn_mfma_bwd.hip", "abi.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed FP32 instructions are switched off for device code (the host pass of hipcc warns that
@@ -31,7 +31,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
 
 # Matrix-core accumulators in VGPRs (not AGPRs) so the softmax rescale of the output
 # accumulator needs no AGPR<->VGPR copies.
-EXTRA = {"attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "proj_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "proj_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attn_mfma_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):

@@ -197,6 +197,9 @@ int attamba_kvssm_scan_bwd(const attamba_scan_bwd_args* b, attamba_stream_t stre
       !b->dbm_v || !b->dcm_v || !b->dA_k || !b->dA_v || !b->dD_k || !b->dD_v || !b->dbias_k || !b->dbias_v)
     return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan_bwd: a required gradient pointer is null");
   if (!b->gkb != !b->gvb) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan_bwd: gkb and gvb must both be set or both null");
+  for (const void* ptr : {a->bm_k, a->cm_k, a->bm_v, a->cm_v})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan_bwd: bm/cm pointers must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   attamba::ZeroList z{};
   float* bufs[attamba::kMaxZero] = {b->dbm_k, b->dcm_k, b->dbm_v, b->dcm_v, b->dA_k, b->dA_v,
@@ -238,7 +241,10 @@ int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* b, attamba_stream_t stre
   f.seq_cu = a->seq_cu; f.chunk_cu = a->chunk_cu; f.token_chunk = a->token_chunk;
   f.out = a->out; f.lse = a->lse;
   p.dout = b->dout; p.dq = b->dq; p.dk = b->dk; p.dv = b->dv; p.dkb = b->dkb; p.dvb = b->dvb;
-  p.delta = b->workspace; p.n_chunks = a->n_chunks;
+  p.delta = b->workspace;
+  p.row_w = reinterpret_cast<int*>(b->workspace + static_cast<size_t>(a->H) * a->T);
+  p.row_ce = p.row_w + a->T;
+  p.n_chunks = a->n_chunks;
   return hip_status(attamba::launch_chunk_attn_bwd(p, a->hd, a->dtype, reinterpret_cast<hipStream_t>(stream)),
                     "chunk_attn_bwd launch");
 }

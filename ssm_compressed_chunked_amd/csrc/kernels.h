@@ -80,9 +80,13 @@ struct AttnBwdParams {
   const void* dout;
   void *dq, *dk, *dv, *dkb, *dvb;
   float* delta;                   // [H, T] rowsum(dout * out)
+  int* row_w;                     // [T] first band position w_i of every row
+  int* row_ce;                    // [T] c0 + E_i: first boundary state row i does not see
   int n_chunks;
 };
 hipError_t launch_chunk_attn_bwd(const AttnBwdParams& p, int hd, int dtype, hipStream_t stream);
+// bf16 matrix-core backward for hd 64 and 128 (needs delta, row_w and row_ce filled).
+hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, int hd, hipStream_t stream);
 
 int decode_max_splits(int cap, int L);
 size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L);

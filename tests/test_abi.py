@@ -164,3 +164,6 @@ def test_backward_entry_points_validate_before_launch():
         setattr(s, name, fake)
     s.gkb = fake
     assert lib.attamba_kvssm_scan_bwd(C.byref(s), None) == B.ERR_NULL_ARG   # gkb without gvb
+    s.gkb = None
+    a.bm_v = C.c_void_p(0x1008)
+    assert lib.attamba_kvssm_scan_bwd(C.byref(s), None) == B.ERR_BAD_SHAPE  # misaligned Bm
