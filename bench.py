@@ -425,6 +425,66 @@ def bench_layer(args):
                    "head_dim": hd, "N": N, "P": cfg.P, "L": cfg.L}}), flush=True)
 
 
+def cpu_baseline_train(cfg, inp, dout, T_full, scan_budget_s=3.0, attn_budget_s=8.0):
+    """The oracle's forward and backward on a bounded sample of the training workload: both
+    scans and their backward over a whole-chunk prefix of sequence 0 (all channels), and the
+    attention forward and backward of sequence 0 for as many heads as fit in about
+    attn_budget_s; scaled to the whole batch like cpu_baseline."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    f = {k: inp.f64(k) for k in list(inp.act) + list(inp.param)}
+    chunk_cu, tc, ie = oracle.segment(inp.seq_cu, cfg.P, cfg.layer_idx)
+    s0, s1 = int(inp.seq_cu[0]), int(inp.seq_cu[1])
+    rng = np.random.default_rng(0)
+
+    def scan_prefix(n_tok):
+        n_tok = int(chunk_cu[np.searchsorted(chunk_cu, min(n_tok, s1))])
+        cu = chunk_cu[chunk_cu <= n_tok]
+        t0 = time.perf_counter()
+        for tag in ("k", "v"):
+            args = (f["x"][:n_tok], f[f"dt_{tag}"][:n_tok], f[f"bias_{tag}"], f[f"A_{tag}"],
+                    f[f"bm_{tag}"][:n_tok], f[f"cm_{tag}"][:n_tok], f[f"D_{tag}"], cu)
+            oracle.selective_scan(*args)
+            oracle.selective_scan_backward(*args, rng.standard_normal((n_tok, cfg.d)))
+        return n_tok, time.perf_counter() - t0
+
+    n_scan, t_scan = scan_prefix(256)
+    if t_scan < scan_budget_s and n_scan < s1:
+        n_scan, t_scan = scan_prefix(int(n_scan * scan_budget_s / max(t_scan, 1e-3)))
+    H, hd = cfg.H, cfg.hd
+    t_attn, heads = 0.0, 0
+    n = s1 - s0
+    while heads < H and t_attn < attn_budget_s:
+        q = f["q"][s0:s1].reshape(-1, H, hd)[:, heads:heads + 1]
+        k = rng.standard_normal((n, 1, hd))
+        v = rng.standard_normal((n, 1, hd))
+        g = dout[s0:s1, heads:heads + 1].to(dtype=__import__("torch").float64).numpy()
+        t0 = time.perf_counter()
+        oracle.chunk_attention(q, k, v, [0, n], tc[s0:s1] - tc[s0], ie[s0:s1], cfg.L, cfg.mode)
+        oracle.chunk_attention_backward(q, k, v, [0, n], tc[s0:s1] - tc[s0], ie[s0:s1], cfg.L,
+                                        cfg.mode, g)
+        t_attn += time.perf_counter() - t0
+        heads += 1
+    n_pairs = (len(inp.seq_cu) - 1) * H
+    est = t_scan * (T_full / n_scan) + t_attn / heads * n_pairs
+    return {"value": T_full / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle forward + backward of both scans over tokens 0..{n_scan - 1} of sequence 0 "
+                       f"(all {cfg.d} channels: {t_scan:.2f} s) scaled by {T_full / n_scan:.2f}; oracle attention "
+                       f"forward + backward of sequence 0, heads 0..{heads - 1} ({n} rows each: {t_attn:.2f} s) "
+                       f"scaled to {n_pairs} sequence-head pairs; estimated {est:.1f} s per step")}
+
+
+# minimal VALU slots per state update of the scan backward: the forward recompute (decay
+# multiply, v_exp_f32 at 2.75 slots, input multiply, state FMA), g h for dCm, and the reverse
+# step (dh FMA, dBm multiply, du FMA, decay recomputed, dh e, w = dh e h_prev, dA and ddelta
+# FMAs), plus one add each for the channel sums of dCm and dBm
+SLOTS_PER_UPDATE_BWD = 5.75 + 1.0 + 10.75 + 2.0
+
+
 def bench_train(args):
     """One training step of the KV-SSM path at the M_train workload (bf16, B=4, n=2048,
     d=1024, 16 heads x 64, N=16, P=8, L=64, layer 3): segmentation, both scans, the attention
@@ -432,51 +492,79 @@ def bench_train(args):
     gradient. Phase times come from HIP events on the launch stream."""
     import torch
     import ssm_compressed_chunked_amd as att
-    from ssm_compressed_chunked_amd.pipeline import prefill_backward, prefill_forward
+    from ssm_compressed_chunked_amd.pipeline import prefill_forward
     from workloads import PREFILL_CONFIGS, make_output_grad, make_prefill
     cfg = PREFILL_CONFIGS["train_bf16"]
-    T, H, hd = cfg.T, cfg.H, cfg.hd
+    T, d, H, hd, N = cfg.T, cfg.d, cfg.H, cfg.hd, cfg.N
     inp = make_prefill(cfg)
     act = {k: v.cuda() for k, v in inp.act.items()}
     par = {k: v.cuda() for k, v in inp.param.items()}
     act["seq_cu"] = torch.from_numpy(inp.seq_cu).cuda()
-    dout = make_output_grad((T, H, hd), cfg.dtype, seed=42).cuda()
+    dout_h = make_output_grad((T, H, hd), cfg.dtype, seed=42)
+    dout = dout_h.cuda()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    phase = np.zeros(2)
+    ws = torch.empty((H + 2, T), dtype=torch.float32, device="cuda")
 
-    def step(record=False):
-        if record:
+    def step(ev=None):
+        if ev is not None:
             ev[0].record(stream)
         res = prefill_forward(act, par, inp.seq_cu, H, hd, cfg.P, cfg.layer_idx, cfg.L,
                               att.MASK_TRAIN, stream=stream)
-        if record:
+        if ev is not None:
             ev[1].record(stream)
-        prefill_backward(res, act, par, dout, H, hd, cfg.L, att.MASK_TRAIN, stream=stream)
-        if record:
+        lay, sc, n = res["layout"], res["scan"], res["layout"].n_chunks
+        ga = att.chunk_attn_bwd(act["q"].view(T, H, hd), sc["y_k"].view(T, H, hd),
+                                sc["y_v"].view(T, H, hd), sc["kb"].view(n, H, hd),
+                                sc["vb"].view(n, H, hd), res["seq_cu"], lay.chunk_cu,
+                                lay.token_chunk, res["max_len"], cfg.L, att.MASK_TRAIN,
+                                res["out"], res["lse"], dout, workspace=ws, stream=stream)
+        if ev is not None:
             ev[2].record(stream)
+        att.kvssm_scan_bwd(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"],
+                           act["bm_v"], act["cm_v"], par["A_k"], par["A_v"], par["D_k"],
+                           par["D_v"], par["bias_k"], par["bias_v"], lay.chunk_cu,
+                           ga["dk"].view(T, d), ga["dv"].view(T, d), gkb=ga["dkb"].view(n, d),
+                           gvb=ga["dvb"].view(n, d), stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(record=True)
-        ev[2].synchronize()
-        phase += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])]
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    print(json.dumps({
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    fwd_ms, abwd_ms, sbwd_ms = (float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                                for i in range(3))
+    updates = 2 * T * d * N
+    alu_peak = VALU_SLOTS_PER_S / 1e12
+    ach = SLOTS_PER_UPDATE_BWD * updates / (sbwd_ms * 1e-3) / 1e12
+    line = {
         "metric": "tokens/sec, KV-SSM forward + backward (training step)",
         "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "phases_ms": {"forward": round(phase[0] / args.steps, 4),
-                      "backward": round(phase[1] / args.steps, 4)},
-        "config": {"workload": "train_step_bf16", "B": cfg.B, "n": cfg.n, "d_model": cfg.d,
-                   "heads": H, "head_dim": hd, "N": cfg.N, "P": cfg.P, "L": cfg.L,
-                   "layer_idx": cfg.layer_idx, "mask": "M_train"}}), flush=True)
+        "config": {"workload": "train_step_bf16", "B": cfg.B, "n": cfg.n, "d_model": d,
+                   "heads": H, "head_dim": hd, "N": N, "P": cfg.P, "L": cfg.L,
+                   "layer_idx": cfg.layer_idx, "mask": "M_train+window"},
+        "roofline": {"bound": "alu", "kernel": "kvssm_scan_bwd_kernel", "achieved": round(ach, 3),
+                     "peak": round(alu_peak, 3), "unit": "T VALU-slot/s", "frac": round(ach / alu_peak, 4),
+                     "traffic": None,
+                     "work_per_launch": f"{updates} state updates x {SLOTS_PER_UPDATE_BWD} slots",
+                     "avg_launch_us": round(sbwd_ms * 1e3, 2)},
+        "phases_us": {"forward": round(fwd_ms * 1e3, 2), "attention_backward": round(abwd_ms * 1e3, 2),
+                      "scan_backward": round(sbwd_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_train(cfg, inp, dout_h, T)
+    print(json.dumps(line), flush=True)
 
 
 def bench_copy(args):
