@@ -204,30 +204,33 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
     }
     const int r0 = ia + t * BM;
     const int rl = min(r0 + BM - 1, s1 - 1);
+    // visibility of the wave's keys from the tile's first and last rows (w_i and E_i grow
+    // with i), read from the tile's per-row data in LDS
     bool skip, full;
     if (bnd) {
-      skip = row_ce[rl] <= kw0;
-      full = row_ce[r0] > kw1;
+      skip = sm.ce[buf][rl - r0] <= kw0;
+      full = sm.ce[buf][0] > kw1;
     } else {
-      skip = rl < kw0 || row_w[r0] > kw1;
-      full = row_w[rl] <= kw0 && r0 >= kw1;
+      skip = rl < kw0 || sm.wr[buf][0] > kw1;
+      full = sm.wr[buf][rl - r0] <= kw0 && r0 >= kw1;
     }
     if (wave_live && !skip) {
       const __bf16* sq = sm.q[buf];
       const __bf16* sg = sm.g[buf];
+      // S and dP of both 32-row blocks first: four independent accumulation chains
+      f32x16 sacc[2] = {}, dpacc[2] = {};
+#pragma unroll
+      for (int st = 0; st < QS; ++st)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sq + aoff[st] + 32 * HD * qb);
+          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[st], sacc[qb], 0, 0, 0);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sg + aoff[st] + 32 * HD * qb);
+          dpacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[st], dpacc[qb], 0, 0, 0);
+        }
+      bf16x8 pk[4], dk8[4];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sacc = {}, dpacc = {};
-#pragma unroll
-        for (int st = 0; st < QS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sq + aoff[st] + 32 * HD * qb);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[st], sacc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int st = 0; st < QS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sg + aoff[st] + 32 * HD * qb);
-          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[st], dpacc, 0, 0, 0);
-        }
         float pv[16], dsv[16];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -246,30 +249,27 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g4 + e;
-            float pr = hw_exp2(fmaf(sacc[v], c, -l2a[e]));
+            float pr = hw_exp2(fmaf(sacc[qb][v], c, -l2a[e]));
             if (!full) {
               const bool vis = bnd ? (kx < cea[e]) : (wa[e] <= kx && kx <= r0 + rb + e);
               pr = vis ? pr : 0.f;
             }
             pv[v] = pr;
-            dsv[v] = pr * (dpacc[v] - dda[e]);
+            dsv[v] = pr * (dpacc[qb][v] - dda[e]);
           }
         }
-        bf16x8 pk[2], dk8[2];
-        pack2(pv, pk);
-        pack2(dsv, dk8);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int ks = 2 * qb + kk;
-#pragma unroll
-          for (int j = 0; j < OB; ++j) {
-            const bf16x8 ga = tr_read<HD>(sg, toff[j][0] + 16 * HD * ks, toff[j][1] + 16 * HD * ks);
-            dva[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pk[kk], dva[j], 0, 0, 0);
-            const bf16x8 qa = tr_read<HD>(sq, toff[j][0] + 16 * HD * ks, toff[j][1] + 16 * HD * ks);
-            dka[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dk8[kk], dka[j], 0, 0, 0);
-          }
-        }
+        pack2(pv, *reinterpret_cast<bf16x8(*)[2]>(&pk[2 * qb]));
+        pack2(dsv, *reinterpret_cast<bf16x8(*)[2]>(&dk8[2 * qb]));
       }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < OB; ++j) {
+          const bf16x8 ga = tr_read<HD>(sg, toff[j][0] + 16 * HD * ks, toff[j][1] + 16 * HD * ks);
+          dva[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pk[ks], dva[j], 0, 0, 0);
+          const bf16x8 qa = tr_read<HD>(sq, toff[j][0] + 16 * HD * ks, toff[j][1] + 16 * HD * ks);
+          dka[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dk8[ks], dka[j], 0, 0, 0);
+        }
     }
     if (wid == 0 && t + 1 < nq) meta_store(t + 1);
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of tile t + 1 have landed ...
