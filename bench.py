@@ -234,7 +234,8 @@ def bench_prefill(args):
     scan_alu_tslots = scan_slots / (scan_ms * 1e-3) / 1e12
     alu_peak = VALU_SLOTS_PER_S / 1e12
     traffic = measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"])
-    attn_traffic = measured_traffic("attn_mfma_kernel", ["attn_mfma.hip", "common.h"])
+    attn_traffic = measured_traffic("attn_mfma_kernel", ["attn_mfma.hip", "attn_geom.h", "attn_tiles.h",
+                                                         "common.h"])
     roofline = {"bound": "alu", "kernel": "kvssm_scan_kernel", "achieved": round(scan_alu_tslots, 3),
                 "peak": round(alu_peak, 3), "unit": "T VALU-slot/s", "frac": round(scan_alu_tslots / alu_peak, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
@@ -545,6 +546,7 @@ def bench_train(args):
     updates = 2 * T * d * N
     alu_peak = VALU_SLOTS_PER_S / 1e12
     ach = SLOTS_PER_UPDATE_BWD * updates / (sbwd_ms * 1e-3) / 1e12
+    traffic = measured_traffic("kvssm_scan_bwd_kernel", ["kvssm_scan_bwd.hip", "common.h"])
     line = {
         "metric": "tokens/sec, KV-SSM forward + backward (training step)",
         "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -556,7 +558,7 @@ def bench_train(args):
                    "layer_idx": cfg.layer_idx, "mask": "M_train+window"},
         "roofline": {"bound": "alu", "kernel": "kvssm_scan_bwd_kernel", "achieved": round(ach, 3),
                      "peak": round(alu_peak, 3), "unit": "T VALU-slot/s", "frac": round(ach / alu_peak, 4),
-                     "traffic": None,
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "work_per_launch": f"{updates} state updates x {SLOTS_PER_UPDATE_BWD} slots",
                      "avg_launch_us": round(sbwd_ms * 1e3, 2)},
         "phases_us": {"forward": round(fwd_ms * 1e3, 2), "attention_backward": round(abwd_ms * 1e3, 2),
