@@ -44,9 +44,9 @@ struct DkvSmem {
   int ce[2][BM];           // c0 + E_i (first boundary state not seen)
 };
 
-// 16 accumulator values of one 32-row block, rounded to bf16 and packed as two B operands
-// (k-steps 2 qb and 2 qb + 1: rows 16 kk + {4 hf .. +3, 8 + 4 hf .. +3}).
-__device__ __forceinline__ void pack2(const float (&v)[16], bf16x8 (&out)[2]) {
+// 16 accumulator values of one 32-row block, rounded to bf16 and packed as the B operands of
+// k-steps 2 qb and 2 qb + 1 (rows 16 kk + {4 hf .. +3, 8 + 4 hf .. +3}): out[0] and out[1].
+__device__ __forceinline__ void pack2(const float (&v)[16], bf16x8* out) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
             dsv[v] = pr * (dpacc[qb][v] - dda[e]);
           }
         }
-        pack2(pv, *reinterpret_cast<bf16x8(*)[2]>(&pk[2 * qb]));
-        pack2(dsv, *reinterpret_cast<bf16x8(*)[2]>(&dk8[2 * qb]));
+        pack2(pv, pk + 2 * qb);
+        pack2(dsv, dk8 + 2 * qb);
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)

@@ -17,12 +17,11 @@
 // of SSM_K or of SSM_V; a workgroup = 4 waves = 128 channels of one SSM over one group of whole
 // chunks. A chunk is walked backwards in blocks of PB tokens: the block's Bm/Cm rows (the same
 // for every channel) are staged once in LDS, its states are recomputed forward from the chunk
-// start and kept in VGPRs, then the block is walked in reverse. The two
-// halves of a channel meet with one cross-lane swap for the sums over n (dh . Bm and the decay
-// term of ddelta). The channel sums dCm (forward pass) and dBm (reverse pass) are reduced across
-// the 32 lanes of each half with
-// cross-lane swaps and DPP moves (every lane ends with one summed quantity), across the
-// workgroup's waves in LDS, and added to the [T, N] outputs with one float atomic per
+// start and kept in VGPRs, then the block is walked in reverse. The two halves of a channel meet
+// with one cross-lane swap for the sums over n (dh . Bm and the decay term of ddelta). The
+// channel sums dCm (forward pass) and dBm (reverse pass) are reduced across the 32 lanes of each
+// half with cross-lane swaps and DPP moves (every lane ends with one summed quantity), across
+// the workgroup's waves in LDS, and added to the [T, N] outputs with one float atomic per
 // (token, n) per workgroup; the per-channel parameter gradients are accumulated in VGPRs over
 // the chunk group and added with float atomics at its end, so results carry float
 // reassociation, not bit-for-bit repeatability.

@@ -291,3 +291,89 @@ def test_full_size_train_chain_sampled():
         a, b = int(inp.seq_cu[s]), int(inp.seq_cu[s + 1])
         for key in ("dq", "dx_k", "dx_v", "ddt_k", "ddt_v", "dbm_k", "dcm_v"):
             assert not g[key][a:b].any(), (key, s)
+
+
+def test_full_size_random_chunks_sampled():
+    """The random-chunk workload at full size (B=2, n=8192, d=2048, 32 heads x 64, chunk lengths
+    2..16, M_test + window), in the launch configuration of the full workload: chunks longer
+    than one register block take the multi-block path of the scan backward. Output gradients are
+    nonzero on the second sequence only. The scan backward is checked on all its channels and
+    every parameter-gradient sum; the attention backward on heads 0 and 17 of that sequence. The
+    first sequence's gradients must be exactly zero."""
+    cfg = VARCHUNK_BF16
+    say(f"full-size random chunks {cfg.name}")
+    inp = make_prefill(cfg)
+    T, d, H, hd = cfg.T, cfg.d, cfg.H, cfg.hd
+    a1 = int(inp.seq_cu[1])
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    par = {k: v.cuda() for k, v in inp.param.items()}
+    seq_cu, lay, ref_lay = _layout(inp, cfg, True)
+    n = lay.n_chunks
+    cu = ref_lay[0]
+    q1 = int(np.searchsorted(cu, a1))                    # first chunk of sequence 1
+    gy = {t: make_output_grad((T, d), cfg.dtype, seed=50 + i) for i, t in enumerate("kv")}
+    gb = {t: make_output_grad((n, d), cfg.dtype, seed=60 + i) for i, t in enumerate("kv")}
+    for t in "kv":
+        gy[t][:a1] = 0
+        gb[t][:q1] = 0
+    g = att.kvssm_scan_bwd(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"], act["bm_v"],
+                           act["cm_v"], par["A_k"], par["A_v"], par["D_k"], par["D_v"], par["bias_k"],
+                           par["bias_v"], lay.chunk_cu, gy["k"].cuda(), gy["v"].cuda(),
+                           gkb=gb["k"].cuda(), gvb=gb["v"].cuda())
+    # attention on seeded q, k, v with kb, vb = k, v at the chunk ends
+    qa, ka, va = (make_output_grad((T, H, hd), cfg.dtype, seed=s).cuda() for s in (71, 72, 73))
+    dout = make_output_grad((T, H, hd), cfg.dtype, seed=74)
+    dout[:a1] = 0
+    ends = torch.from_numpy(np.asarray(cu[1:], dtype=np.int64) - 1).cuda()
+    kb, vb = ka[ends].contiguous(), va[ends].contiguous()
+    max_len = int(np.diff(inp.seq_cu).max())
+    out, lse = att.chunk_attn_fwd(qa, ka, va, kb, vb, seq_cu, lay.chunk_cu, lay.token_chunk, max_len, cfg.L,
+                                  MODE[cfg.mode])
+    ga = att.chunk_attn_bwd(qa, ka, va, kb, vb, seq_cu, lay.chunk_cu, lay.token_chunk, max_len, cfg.L,
+                            MODE[cfg.mode], out, lse, dout.cuda())
+    torch.cuda.synchronize()
+    say("  GPU done; oracle scan backward of sequence 1")
+    for key in ("dx_k", "dx_v", "ddt_k", "ddt_v", "dbm_k", "dcm_v"):
+        assert not g[key][:a1].any(), key
+    for key in ("dq", "dk", "dv"):
+        assert not ga[key][:a1].any(), key
+    cu1 = cu[q1:] - a1
+    for t in "kv":
+        gyt = _scatter_ends(gy[t][a1:].to(torch.float64).numpy(), gb[t][q1:].to(torch.float64).numpy(), cu1)
+        ref = oracle.selective_scan_backward(inp.f64("x")[a1:], inp.f64(f"dt_{t}")[a1:], inp.f64(f"bias_{t}"),
+                                             inp.f64(f"A_{t}"), inp.f64(f"bm_{t}")[a1:], inp.f64(f"cm_{t}")[a1:],
+                                             inp.f64(f"D_{t}"), cu1, gyt)
+        for key, mine in (("dx", f"dx_{t}"), ("ddt", f"ddt_{t}"), ("dBm", f"dbm_{t}"), ("dCm", f"dcm_{t}")):
+            is_sum = key not in ("dx", "ddt")
+            check_close(g[mine][a1:].float().cpu().numpy(), ref[key], "fp32" if is_sum else cfg.dtype,
+                        f"{mine} seq 1", sum_output=is_sum)
+        for key, mine in (("dA", f"dA_{t}"), ("dD", f"dD_{t}"), ("dbias", f"dbias_{t}")):
+            check_close(g[mine].float().cpu().numpy(), ref[key], "fp32", mine, sum_output=True)
+    say("  oracle attention backward of sequence 1, heads 0 and 17")
+    f = lambda x: x[a1:].to(torch.float64).cpu().numpy()
+    tc1, ie1 = ref_lay[1][a1:] - ref_lay[1][a1], ref_lay[2][a1:]
+    for h in (0, 17):
+        sl = slice(h, h + 1)
+        dq, dk, dv = oracle.chunk_attention_backward(f(qa)[:, sl], f(ka)[:, sl], f(va)[:, sl], [0, T - a1], tc1,
+                                                     ie1, cfg.L, cfg.mode, f(dout)[:, sl])
+        check_close(ga["dq"][a1:, sl].float().cpu().numpy(), dq, cfg.dtype, f"dq head {h}")
+        dk_tot = _scatter_ends(ga["dk"][a1:, sl].float().cpu().numpy(), ga["dkb"][q1:, sl].float().cpu().numpy(), cu1)
+        dv_tot = _scatter_ends(ga["dv"][a1:, sl].float().cpu().numpy(), ga["dvb"][q1:, sl].float().cpu().numpy(), cu1)
+        check_close(dk_tot, dk, cfg.dtype, f"dk head {h}")
+        check_close(dv_tot, dv, cfg.dtype, f"dv head {h}")
+
+
+def test_chain_hd128_N32():
+    """bf16, head dim 128 (the matrix-core backward at hd 128) with state size 32 (two-token
+    register blocks in the scan backward), M_train with a window."""
+    cfg, inp = _inputs(TRAIN_BF16, dict(d=256, H=2, hd=128, N=32, P=6, L=40, layer_idx=2), [300, 97], False)
+    T = int(inp.seq_cu[-1])
+    say(f"chain hd128 N32: T={T}")
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    par = {k: v.cuda() for k, v in inp.param.items()}
+    dout = make_output_grad((T, cfg.H, cfg.hd), cfg.dtype, seed=44)
+    res = prefill_forward(act, par, inp.seq_cu, cfg.H, cfg.hd, cfg.P, cfg.layer_idx, cfg.L, MODE[cfg.mode])
+    g = prefill_backward(res, act, par, dout.cuda(), cfg.H, cfg.hd, cfg.L, MODE[cfg.mode])
+    torch.cuda.synchronize()
+    ref = _oracle_chain(inp, cfg, cfg.P, dout.to(torch.float64).numpy(), range(len(inp.seq_cu) - 1))
+    _compare_chain(g, ref, inp, cfg, list(ref))
