@@ -249,6 +249,35 @@ int attamba_decode_workspace_size(const attamba_decode_cache* cache, size_t* byt
 int attamba_decode_step(attamba_decode_cache* cache, const attamba_decode_inputs* in,
                         attamba_stream_t stream);
 
+/* Prefill -> decode hand-off (pith.science "Core claim": at inference only the boundary states
+ * are cached; a model serves a prompt by prefilling it and then decoding). A batch of S = B
+ * sequences, each of exactly n0 tokens, was prefilled with uniform chunking of the cache's P
+ * and layer_idx (attamba_chunk_boundaries, then attamba_kvssm_scan with h_last). This call
+ * copies into the cache, for every sequence: the boundary states of the chunks that end before
+ * n0 (the first ends_before(n0) chunks of the sequence; a trailing partial chunk lives on in h),
+ * the per-token keys and values of the window positions max(0, n0 - L) .. n0 - 1 (slot
+ * position mod L), and the SSM states after the last prefix token; then sets cache->pos = n0
+ * and cache->n_bound. The cache keeps its other fields. All tensors are device pointers except
+ * seq_cu_host. Errors: NULL_ARG; BAD_SHAPE (S != B, a sequence not n0 tokens long, n0 < 0, or the
+ * cache geometry invalid as for attamba_decode_step); CAPACITY (more completed chunks than
+ * cap); BAD_DTYPE; UNSUPPORTED (hd, N, d as for attamba_decode_step); HIP. */
+typedef struct {
+  int32_t S;                    /* sequences (must equal cache->B) */
+  int32_t n0;                   /* prefix length of every sequence */
+  const int32_t* seq_cu_host;   /* [S + 1] host copy of seq_cu */
+  const int32_t* seq_cu;        /* [S + 1] device */
+  const int32_t* token_chunk;   /* [T] device: the prefill's chunk of every token */
+  const void* y_k;              /* [T, d] prefill per-token keys (cache dtype) */
+  const void* y_v;              /* [T, d] */
+  const void* kb;               /* [n_chunks, d] prefill boundary keys */
+  const void* vb;               /* [n_chunks, d] */
+  const float* h_last_k;        /* [S, d, N] SSM_K state after each sequence's last token */
+  const float* h_last_v;        /* [S, d, N] */
+} attamba_decode_prefix;
+
+int attamba_decode_load_prefix(attamba_decode_cache* cache, const attamba_decode_prefix* prefix,
+                               attamba_stream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Input projections (the step just before the path: the queries and the per-token inputs
  * dt, Bm, Cm of SSM_K and SSM_V are linear maps of the layer input; pith.science "Core claim":

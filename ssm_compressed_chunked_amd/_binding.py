@@ -52,6 +52,12 @@ class AttnArgs(C.Structure):
                 ("out", _vp), ("lse", _vp)]
 
 
+class DecodePrefixStruct(C.Structure):
+    _fields_ = [("S", _i32), ("n0", _i32), ("seq_cu_host", _i32p), ("seq_cu", _vp),
+                ("token_chunk", _vp), ("y_k", _vp), ("y_v", _vp), ("kb", _vp), ("vb", _vp),
+                ("h_last_k", _vp), ("h_last_v", _vp)]
+
+
 class AttnBwdArgs(C.Structure):
     _fields_ = [("fwd", AttnArgs), ("dout", _vp), ("dq", _vp), ("dk", _vp), ("dv", _vp),
                 ("dkb", _vp), ("dvb", _vp), ("workspace", _vp)]
@@ -93,6 +99,8 @@ EXPORTS = {
                                       C.c_int),
     "attamba_decode_step": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodeInputsStruct), _vp],
                             C.c_int),
+    "attamba_decode_load_prefix": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodePrefixStruct), _vp],
+                                   C.c_int),
     "attamba_chunk_attn_bwd": ([C.POINTER(AttnBwdArgs), _vp], C.c_int),
     "attamba_kvssm_scan_bwd": ([C.POINTER(ScanBwdArgs), _vp], C.c_int),
 }
@@ -436,6 +444,28 @@ class DecodeCache:
 
     def set_position(self, pos: int, n_bound: int) -> None:
         self.struct.pos, self.struct.n_bound = pos, n_bound
+
+    def load_prefix(self, seq_cu_host, seq_cu, token_chunk, y_k, y_v, kb, vb, h_last_k, h_last_v,
+                    stream=None) -> None:
+        """Fill the cache from a prefill of B sequences of equal length n0 (uniform chunking
+        with this cache's P and layer index; the scan run with h_last): completed boundary
+        states, the last L per-token keys/values and the SSM states. Sets pos = n0."""
+        seq_h = _host_i32(seq_cu_host)
+        S = len(seq_h) - 1
+        d, N = self.d, self.N
+        T = int(seq_h[-1])
+        pf = DecodePrefixStruct()
+        pf.S, pf.n0 = S, int(seq_h[1] - seq_h[0]) if S > 0 else 0
+        pf.seq_cu_host = seq_h.ctypes.data_as(_i32p)
+        pf.seq_cu = _dev(seq_cu, "seq_cu", torch.int32, S + 1)
+        pf.token_chunk = _dev(token_chunk, "token_chunk", torch.int32, T)
+        pf.y_k = _dev(y_k, "y_k", self.dtype, T * d)
+        pf.y_v = _dev(y_v, "y_v", self.dtype, T * d)
+        pf.kb = _dev(kb, "kb", self.dtype)
+        pf.vb = _dev(vb, "vb", self.dtype)
+        pf.h_last_k = _dev(h_last_k, "h_last_k", torch.float32, S * d * N)
+        pf.h_last_v = _dev(h_last_v, "h_last_v", torch.float32, S * d * N)
+        _check(lib().attamba_decode_load_prefix(C.byref(self.struct), C.byref(pf), _stream(stream)))
 
 
 def decode_step(cache: DecodeCache, q, x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, out=None,

@@ -286,6 +286,45 @@ int attamba_decode_workspace_size(const attamba_decode_cache* c, size_t* bytes) 
   return ok();
 }
 
+int attamba_decode_load_prefix(attamba_decode_cache* c, const attamba_decode_prefix* pf,
+                               attamba_stream_t stream) {
+  if (!c || !pf) return fail(ATTAMBA_ERR_NULL_ARG, "decode_load_prefix: null pointer");
+  if (!dtype_ok(c->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "decode_load_prefix: dtype %d", c->dtype);
+  if (c->B < 1 || c->H < 1 || c->P < 1 || c->L < 0 || c->layer_idx < 0 || c->cap < 0 || c->d != c->H * c->hd)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_load_prefix: B=%d H=%d hd=%d d=%d P=%d L=%d cap=%d", c->B, c->H,
+                c->hd, c->d, c->P, c->L, c->cap);
+  if (c->hd != 32 && c->hd != 64 && c->hd != 128)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_load_prefix: hd=%d (32, 64 or 128)", c->hd);
+  if (c->N != 16 && c->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_load_prefix: N=%d (16 or 32)", c->N);
+  if (c->d % 64 != 0) return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_load_prefix: d=%d not a multiple of 64", c->d);
+  if (!pf->seq_cu_host || !pf->seq_cu || !pf->token_chunk || !pf->y_k || !pf->y_v || !pf->kb || !pf->vb ||
+      !pf->h_last_k || !pf->h_last_v || !c->kb || !c->vb || !c->h_k || !c->h_v || (c->L > 0 && (!c->kw || !c->vw)))
+    return fail(ATTAMBA_ERR_NULL_ARG, "decode_load_prefix: a required pointer is null");
+  if (pf->S != c->B || pf->n0 < 0)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_load_prefix: S=%d (cache B=%d), n0=%d", pf->S, c->B, pf->n0);
+  if (pf->seq_cu_host[0] != 0)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_load_prefix: seq_cu must start at 0");
+  for (int s = 0; s < pf->S; ++s)
+    if (pf->seq_cu_host[s + 1] - pf->seq_cu_host[s] != pf->n0)
+      return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_load_prefix: sequence %d has %d tokens, not n0=%d", s,
+                  pf->seq_cu_host[s + 1] - pf->seq_cu_host[s], pf->n0);
+  if (static_cast<int64_t>(pf->seq_cu_host[pf->S]) * c->d > INT32_MAX)
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_load_prefix: T*d exceeds 2^31 elements");
+  const int64_t P = c->P, o = c->layer_idx % c->P;
+  const int64_t n_bound = ends_before(pf->n0, P, o);
+  if (n_bound > c->cap)
+    return fail(ATTAMBA_ERR_CAPACITY, "decode_load_prefix: %lld completed chunks exceed cap=%d",
+                static_cast<long long>(n_bound), c->cap);
+  const int w0 = c->L > 0 ? (pf->n0 - c->L > 0 ? pf->n0 - c->L : 0) : pf->n0;
+  const int st = hip_status(attamba::launch_decode_load_prefix(*c, *pf, static_cast<int>(n_bound), w0,
+                                                               reinterpret_cast<hipStream_t>(stream)),
+                            "decode_load_prefix launch");
+  if (st != ATTAMBA_OK) return st;
+  c->pos = pf->n0;
+  c->n_bound = static_cast<int32_t>(n_bound);
+  return ATTAMBA_OK;
+}
+
 int attamba_decode_step(attamba_decode_cache* c, const attamba_decode_inputs* in,
                         attamba_stream_t stream) {
   if (!c || !in) return fail(ATTAMBA_ERR_NULL_ARG, "decode_step: null pointer");

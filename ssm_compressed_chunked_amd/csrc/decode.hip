@@ -294,7 +294,67 @@ hipError_t launch_hd(const attamba_decode_cache& c, const attamba_decode_inputs&
   return launch_typed<T, N, 32>(c, in, dl, stream);
 }
 
+// Prefill -> decode hand-off: block (b, h) copies the n_bound completed boundary states of
+// sequence b (its chunks c_b .. c_b + n_bound - 1 of the prefill) and the per-token keys/values
+// of the window positions w0 .. n0 - 1 into the head-major cache rows.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_load_prefix_kernel(attamba_decode_cache c,
+                                                                 attamba_decode_prefix pf,
+                                                                 int n_bound, int w0) {
+  const int bh = blockIdx.x;
+  const int b = bh / c.H, h = bh % c.H;
+  const int hd = c.hd, d = c.d;
+  const int s0 = pf.seq_cu[b];
+  const int cb = pf.token_chunk[s0];
+  const int rows = n_bound + (pf.n0 - w0);
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  if (e >= rows * hd) return;
+  const int r = e / hd, k = e % hd;
+  const size_t head = static_cast<size_t>(b) * c.H + h;
+  const T* sk;
+  const T* sv;
+  T* dk;
+  T* dv;
+  size_t so, dof;
+  if (r < n_bound) {
+    so = static_cast<size_t>(cb + r) * d + h * hd + k;
+    dof = (head * c.cap + r) * hd + k;
+    sk = static_cast<const T*>(pf.kb); sv = static_cast<const T*>(pf.vb);
+    dk = static_cast<T*>(c.kb); dv = static_cast<T*>(c.vb);
+  } else {
+    const int pos = w0 + (r - n_bound);
+    so = static_cast<size_t>(s0 + pos) * d + h * hd + k;
+    dof = (head * c.L + pos % c.L) * hd + k;
+    sk = static_cast<const T*>(pf.y_k); sv = static_cast<const T*>(pf.y_v);
+    dk = static_cast<T*>(c.kw); dv = static_cast<T*>(c.vw);
+  }
+  dk[dof] = sk[so];
+  dv[dof] = sv[so];
+}
+
+__global__ __launch_bounds__(256) void copy_f32_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                       size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
+    dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_decode_load_prefix(const attamba_decode_cache& c, const attamba_decode_prefix& pf,
+                                     int n_bound, int w0, hipStream_t stream) {
+  const int rows = n_bound + (pf.n0 - w0);
+  if (rows > 0) {
+    const dim3 grid(c.B * c.H, ceil_div(rows * c.hd, 256));
+    if (c.dtype == ATTAMBA_BF16)
+      hipLaunchKernelGGL(decode_load_prefix_kernel<__bf16>, grid, dim3(256), 0, stream, c, pf, n_bound, w0);
+    else
+      hipLaunchKernelGGL(decode_load_prefix_kernel<float>, grid, dim3(256), 0, stream, c, pf, n_bound, w0);
+  }
+  const size_t n = static_cast<size_t>(c.B) * c.d * c.N;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(1024), dim3(256), 0, stream, c.h_k, pf.h_last_k, n);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(1024), dim3(256), 0, stream, c.h_v, pf.h_last_v, n);
+  return hipGetLastError();
+}
 
 int decode_max_splits(int cap, int L) { return ceil_div(cap + L, kSplit) + 1; }
 

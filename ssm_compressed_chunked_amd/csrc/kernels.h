@@ -92,5 +92,7 @@ int decode_max_splits(int cap, int L);
 size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L);
 hipError_t launch_decode_step(const attamba_decode_cache& c, const attamba_decode_inputs& in,
                               const DecodeLaunch& dl, hipStream_t stream);
+hipError_t launch_decode_load_prefix(const attamba_decode_cache& c, const attamba_decode_prefix& pf,
+                                     int n_bound, int w0, hipStream_t stream);
 
 }  // namespace attamba

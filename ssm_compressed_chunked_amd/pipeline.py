@@ -36,9 +36,10 @@ def chunk_layout(seq_cu_host, seq_cu: torch.Tensor, T: int, P: int | None, layer
 
 def prefill_forward(act: dict, params: dict, seq_cu_host, H: int, hd: int, P: int | None,
                     layer_idx: int, L: int, mode: int, chunk_lens=None, layout=None,
-                    stream=None, want_lse: bool = True) -> dict:
+                    stream=None, want_lse: bool = True, h_last: bool = False) -> dict:
     """act: device tensors x, q, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v; params: A_k, A_v, D_k,
-    D_v, bias_k, bias_v (float32). Returns the layout, the scan outputs and (out, lse)."""
+    D_v, bias_k, bias_v (float32). Returns the layout, the scan outputs and (out, lse).
+    h_last: also return the SSM states after each sequence's last token (decode hand-off)."""
     x = act["x"]
     T, d = x.shape
     seq_cu_host = np.asarray(seq_cu_host, dtype=np.int32)
@@ -50,7 +51,8 @@ def prefill_forward(act: dict, params: dict, seq_cu_host, H: int, hd: int, P: in
     scan = B.kvssm_scan(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"],
                         act["bm_v"], act["cm_v"], params["A_k"], params["A_v"], params["D_k"],
                         params["D_v"], params["bias_k"], params["bias_v"], layout.chunk_cu,
-                        x_v=act.get("x_v"), stream=stream)
+                        x_v=act.get("x_v"), seq_cu=seq_cu if h_last else None, h_last=h_last,
+                        stream=stream)
     max_len = int(np.max(np.diff(seq_cu_host))) if len(seq_cu_host) > 1 else 0
     n = layout.n_chunks
     out, lse = B.chunk_attn_fwd(act["q"].view(T, H, hd), scan["y_k"].view(T, H, hd),
@@ -86,6 +88,21 @@ def prefill_backward(res: dict, act: dict, params: dict, dout: torch.Tensor, H: 
                           ga["dk"].view(T, d), ga["dv"].view(T, d), gkb=ga["dkb"].view(n, d),
                           gvb=ga["dvb"].view(n, d), x_v=act.get("x_v"), stream=stream)
     return {**ga, **gs}
+
+
+def decode_from_prefill(res: dict, seq_cu_host, params: dict, H: int, hd: int, N: int, P: int,
+                        layer_idx: int, L: int, cap: int, stream=None) -> "B.DecodeCache":
+    """A decode cache for one layer, filled on the GPU from that layer's prefill (the result of
+    prefill_forward(..., h_last=True) over sequences of equal length n0, uniform chunking with
+    the same P and layer index). A model keeps one such cache per layer, each with its own
+    cyclic offset; the next token of every layer then goes through decode_step."""
+    x_dtype = res["scan"]["y_k"].dtype
+    B_ = len(seq_cu_host) - 1
+    cache = B.DecodeCache(B_, H, hd, N, P, L, layer_idx, cap, x_dtype, params)
+    sc = res["scan"]
+    cache.load_prefix(seq_cu_host, res["seq_cu"], res["layout"].token_chunk, sc["y_k"], sc["y_v"],
+                      sc["kb"], sc["vb"], sc["h_last_k"], sc["h_last_v"], stream=stream)
+    return cache
 
 
 PROJ_NAMES = ("q", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v")

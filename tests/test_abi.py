@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_and_exports_agree():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert set(names) == set(B.EXPORTS), (set(names) ^ set(B.EXPORTS))
     lib = att.lib()
     for n in names:
@@ -167,3 +167,32 @@ def test_backward_entry_points_validate_before_launch():
     s.gkb = None
     a.bm_v = C.c_void_p(0x1008)
     assert lib.attamba_kvssm_scan_bwd(C.byref(s), None) == B.ERR_BAD_SHAPE  # misaligned Bm
+
+
+def test_decode_load_prefix_validates_before_launch():
+    import numpy as np
+    lib = att.lib()
+    assert lib.attamba_decode_load_prefix(None, None, None) == B.ERR_NULL_ARG
+    fake = C.c_void_p(0x1000)          # never dereferenced: validation fails before any launch
+    c = B.DecodeCacheStruct()
+    c.B, c.H, c.hd, c.d, c.N, c.P, c.L, c.layer_idx, c.cap, c.dtype = 2, 2, 64, 128, 16, 4, 3, 1, 2, 1
+    for name in ("kb", "vb", "kw", "vw", "h_k", "h_v"):
+        setattr(c, name, fake)
+    pf = B.DecodePrefixStruct()
+    seq = np.array([0, 10, 20], dtype=np.int32)
+    pf.S, pf.n0, pf.seq_cu_host = 2, 10, seq.ctypes.data_as(C.POINTER(C.c_int32))
+    for name in ("seq_cu", "token_chunk", "y_k", "y_v", "kb", "vb", "h_last_k", "h_last_v"):
+        setattr(pf, name, fake)
+    assert lib.attamba_decode_load_prefix(C.byref(c), C.byref(pf), None) == B.ERR_CAPACITY  # 3 ends > cap 2
+    c.cap = 8
+    pf.S = 3
+    assert lib.attamba_decode_load_prefix(C.byref(c), C.byref(pf), None) == B.ERR_BAD_SHAPE  # S != B
+    pf.S = 2
+    seq[2] = 19
+    assert lib.attamba_decode_load_prefix(C.byref(c), C.byref(pf), None) == B.ERR_BAD_SHAPE  # ragged
+    seq[2] = 20
+    pf.h_last_v = None
+    assert lib.attamba_decode_load_prefix(C.byref(c), C.byref(pf), None) == B.ERR_NULL_ARG
+    pf.h_last_v = fake
+    c.hd, c.d = 48, 96
+    assert lib.attamba_decode_load_prefix(C.byref(c), C.byref(pf), None) == B.ERR_UNSUPPORTED

@@ -484,3 +484,40 @@ def test_scan_separate_value_input():
     check_close(res["y_k"].float().cpu().numpy(), ref["y_k"], "bf16", "y_k")
     check_close(res["y_v"].float().cpu().numpy(), ref["y_v"], "bf16", "y_v")
     check_close(res["vb"].float().cpu().numpy().reshape(-1, cfg.H, cfg.hd), ref["vb"], "bf16", "vb")
+
+
+# ------------------------------------------------ prefill -> decode, one cache per layer
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_multilayer_prefill_then_decode(dtype):
+    """Serving on the GPU alone: every layer (cyclic offsets 0, 1, 2 at P = 3) prefills a prompt
+    of n0 tokens per sequence, hands the prefill to its own decode cache on the device
+    (attamba_decode_load_prefix: completed boundary states, the last L keys/values, the SSM
+    states) and decodes the next tokens. Each decoded output equals the row of the oracle's
+    prefill over the whole length."""
+    from ssm_compressed_chunked_amd.pipeline import decode_from_prefill
+    B, H, hd, N, P, L, n0, steps = 2, 2, 64, 16, 3, 4, 19, 8
+    n_total = n0 + steps
+    base = PREFILL_BF16 if dtype == "bf16" else TINY_FP32
+    for layer in (0, 1, 2):
+        cfg = base.with_(B=B, n=n_total, d=H * hd, H=H, hd=hd, N=N, P=P, L=L, layer_idx=layer, mode="test")
+        inp = make_prefill(cfg, seed=200 + layer)
+        say(f"multilayer decode dtype={dtype} layer={layer}")
+        ref = oracle.kvssm_forward(f64_inputs(inp), inp.seq_cu, H, hd, P, layer, L, "test")
+        # the prompts: the first n0 tokens of every sequence, packed
+        rows = np.concatenate([np.arange(n0) + int(inp.seq_cu[b]) for b in range(B)])
+        act_full = {k: v.cuda() for k, v in inp.act.items()}
+        act = {k: v[torch.from_numpy(rows).cuda()].contiguous() for k, v in act_full.items()}
+        par = {k: v.cuda() for k, v in inp.param.items()}
+        seq_cu_h = (np.arange(B + 1) * n0).astype(np.int32)
+        res = prefill_forward(act, par, seq_cu_h, H, hd, P, layer, L, att.MASK_TEST, h_last=True)
+        cache = decode_from_prefill(res, seq_cu_h, par, H, hd, N, P, layer, L, cap=n_total // P + 2)
+        assert cache.pos == n0
+        assert cache.n_bound == sum(1 for j in range(n0) if oracle.is_chunk_end_at(j, P, layer))
+        for i in range(n0, n_total):
+            r = torch.from_numpy(inp.seq_cu[:-1] + i).long().cuda()
+            out = att.decode_step(cache, act_full["q"][r].view(B, H, hd).contiguous(),
+                                  *[act_full[k][r].contiguous() for k in ("x", "dt_k", "dt_v", "bm_k", "cm_k",
+                                                                          "bm_v", "cm_v")])
+            torch.cuda.synchronize()
+            check_close(out.float().cpu().numpy(), ref["out"][inp.seq_cu[:-1] + i], dtype,
+                        f"layer {layer} decode pos {i}")
