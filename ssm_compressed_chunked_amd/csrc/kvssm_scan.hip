@@ -3,29 +3,31 @@
 // To Multi-Token States", "Core claim"; the selective SSM is the paper's Eq. 3, cited in
 // "Assumptions & free parameters").
 //
-// SSM_V may read its own input (the variant that keeps explicit key and value projections in
-// front of the SSMs); by default both SSMs read x, loaded once.
-//
-// Mapping on gfx950: one lane owns one channel c of both SSMs and keeps the 2*N state values
-// and the 2*N decay rates (A * log2 e) in VGPRs; a wave owns 64 consecutive channels and walks
-// a group of whole chunks token by token (chunks are independent because the state restarts
-// at every chunk start). All lanes of a wave sit on the same token, so the per-token rows
-// bm/cm (shared by all channels) are wave-uniform: the pointers are restrict-qualified kernel
-// arguments, so they are fetched with scalar loads, widened to float32 on the scalar unit and
-// enter the VALU instructions as SGPR operands. Per state and token the work is one multiply
-// for the exponent, one v_exp_f32, one multiply for the input term, one FMA for the state and
-// one FMA for the output; this instruction stream, not HBM, bounds the kernel.
+// Mapping on gfx950: a wave runs ONE of the two SSMs over 64 consecutive channels and a group
+// of whole chunks (chunks are independent because the state restarts at every chunk start).
+// The K and V waves of the same channels and chunks are launched next to each other on the
+// same XCD, so the input x that both read comes from HBM once. One lane owns one channel and
+// keeps its N state values and N decay rates (A * log2 e) in VGPRs. All lanes of a wave sit on
+// the same token, so the per-token rows bm/cm (shared by all channels) are wave-uniform: they
+// are read through the constant address space as scalar loads, widened to float32 on the
+// scalar unit and enter the VALU instructions as SGPR operands. Per state and token the work
+// is one multiply for the exponent, one v_exp_f32, one multiply for the input term, one FMA
+// for the state and one FMA for the output; this instruction stream, not HBM, bounds the
+// kernel.
+// One SSM per wave (rather than both) halves the scalar registers a token's rows need, which
+// leaves room to request the next token's rows before the current token's arithmetic, and
+// halves the vector registers per lane (about 70: 7 waves per SIMD to hide latency).
 // Chunks of the common length PU are processed fully unrolled: all x/dt loads of the chunk are
 // issued at its start, and no state value is carried across a loop back-edge (it restarts at
 // the next chunk anyway), so no register copies are needed. Other chunk lengths (random
-// chunking, a partial first or last chunk) take a token loop.
+// chunking, a partial first or last chunk) take a token loop with the same one-token prefetch.
 #include "common.h"
 #include "kernels.h"
 
 namespace attamba {
 namespace {
 
-constexpr int kChunksPerWave = 8;
+constexpr int kChunksPerWave = 2;
 
 struct ScanShape {
   int T, d, n_chunks, S;
@@ -33,14 +35,33 @@ struct ScanShape {
   int ctiles;          // channel tiles = d / 64
 };
 
-// Workgroup id -> (chunk group, channel tile). Workgroups are dispatched round-robin over
-// the 8 XCDs (id mod 8), each with its own L2; every channel tile of one chunk group is
-// placed on the same XCD so the group's bm/cm rows are fetched from HBM once per XCD.
-__device__ __forceinline__ bool map_block(const ScanShape& sh, int& group, int& ctile) {
+// The operands of one SSM.
+template <typename T>
+struct SideArgs {
+  const T* x;          // input (SSM_V may read its own)
+  const T* dt;
+  const T* bm;
+  const T* cm;
+  const float* A;
+  const float* D;
+  const float* bias;
+  T* y;
+  T* b;                // boundary outputs or null
+  float* h_last;       // hand-off states or null
+};
+
+// Workgroup id -> (SSM, chunk group, channel tile). Workgroups are dispatched round-robin over
+// the 8 XCDs (id mod 8), each with its own L2; every channel tile and both SSMs of one chunk
+// group are placed on the same XCD, so the group's x and bm/cm rows are fetched from HBM once
+// per XCD, and the K and V waves of one tile are consecutive on that XCD.
+__device__ __forceinline__ bool map_block(const ScanShape& sh, int& side, int& group,
+                                          int& ctile) {
   const int id = blockIdx.x;
   const int xcd = id & 7, slot = id >> 3;
-  group = (slot / sh.ctiles) * 8 + xcd;
-  ctile = slot % sh.ctiles;
+  side = slot & 1;
+  const int tile = slot >> 1;
+  group = (tile / sh.ctiles) * 8 + xcd;
+  ctile = tile % sh.ctiles;
   return group < sh.groups;
 }
 
@@ -59,90 +80,100 @@ struct SsmLane {
     bias = bp[c];
   }
 
-  // One token. FIRST: the state restarts (no decay term). bm/cm point at the token's rows.
-  // The output sum runs in two halves to shorten its dependency chain.
+  // The raw 32-bit words of one token's bm and cm rows (bf16 pairs or float32 values).
+  static constexpr int W = sizeof(T) == 2 ? N / 2 : N;
+  struct Rows {
+    uint32_t b[W], c[W];
+  };
+
+  // Wave-uniform rows, read as 32-bit words through the constant address space: the rows are
+  // never written while the kernel runs, and uniform constant loads become scalar loads.
+  static __device__ __forceinline__ void load_rows(const T* bm, const T* cm, Rows& r) {
+    using cptr = const __attribute__((address_space(4))) uint32_t*;
+    const cptr wb = (cptr)(bm);
+    const cptr wc = (cptr)(cm);
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      r.b[i] = wb[i];
+      r.c[i] = wc[i];
+    }
+  }
+
+  // state n of a row as float32 (bf16 pairs are split with shifts on the scalar unit)
+  static __device__ __forceinline__ float widen(const uint32_t (&w)[W], int n) {
+    if constexpr (sizeof(T) == 2)
+      return __uint_as_float((n & 1) ? (w[n >> 1] & 0xffff0000u) : (w[n >> 1] << 16));
+    else
+      return __uint_as_float(w[n]);
+  }
+
+  // One token. FIRST: the state restarts (no decay term). The output sum runs in two halves
+  // to shorten its dependency chain.
   template <bool FIRST>
-  __device__ __forceinline__ float step(float x, float dt, const T* __restrict__ bm,
-                                        const T* __restrict__ cm) {
-    float b[N], cc[N];
-    load_row(bm, b);
-    load_row(cm, cc);
+  __device__ __forceinline__ float step(float x, float dt, const Rows& r) {
     const float delta = softplus_f32(dt + bias);
     const float u = delta * x;
     float y0 = 0.0f, y1 = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      const float inj = u * b[n];
+      const float inj = u * widen(r.b, n);
       if (FIRST) {
         h[n] = inj;
       } else {
         h[n] = fmaf(hw_exp2(delta * A2[n]), h[n], inj);
       }
-      if (n & 1) y1 = fmaf(h[n], cc[n], y1);
-      else y0 = fmaf(h[n], cc[n], y0);
+      if (n & 1) y1 = fmaf(h[n], widen(r.c, n), y1);
+      else y0 = fmaf(h[n], widen(r.c, n), y0);
     }
     return fmaf(D, x, y0 + y1);
   }
-
-  // A wave-uniform row of N values, read as 32-bit words so that the compiler issues scalar
-  // loads (bf16 pairs are split with shifts on the scalar unit).
-  static __device__ __forceinline__ void load_row(const T* __restrict__ row, float (&v)[N]) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(row);
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int n = 0; n < N / 2; ++n) {
-        const uint32_t p = w[n];
-        v[2 * n] = __uint_as_float(p << 16);
-        v[2 * n + 1] = __uint_as_float(p & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < N; ++n) v[n] = __uint_as_float(w[n]);
-    }
-  }
 };
 
-// SEPX: SSM_V reads its own input xv (explicit key/value projections in front of the SSMs).
-template <typename T, int N, int PU, bool SEPX>
+// Keeps the scalar loads of the next token's rows above the current token's arithmetic (the
+// scheduler would otherwise sink them to their first use and expose their latency).
+__device__ __forceinline__ void order_point() { __builtin_amdgcn_sched_barrier(0); }
+
+// Waits for the current token's rows before the next token's are requested: scalar loads
+// return out of order, so any later wait for them would also wait for the newer requests.
+__device__ __forceinline__ void rows_ready(uint32_t b0, uint32_t c0) {
+  asm volatile("" ::"s"(b0), "s"(c0));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T, int N, int PU>
 __global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
-    ScanShape sh, const int32_t* __restrict__ chunk_cu, const T* __restrict__ x,
-    const T* __restrict__ xv,
-    const T* __restrict__ dtk, const T* __restrict__ dtv, const T* __restrict__ bmk,
-    const T* __restrict__ cmk, const T* __restrict__ bmv, const T* __restrict__ cmv,
-    const float* __restrict__ A_k, const float* __restrict__ A_v, const float* __restrict__ D_k,
-    const float* __restrict__ D_v, const float* __restrict__ bias_k,
-    const float* __restrict__ bias_v, T* __restrict__ yk, T* __restrict__ yv,
-    T* __restrict__ kb, T* __restrict__ vb, const int32_t* __restrict__ seq_cu,
-    float* __restrict__ h_last_k, float* __restrict__ h_last_v) {
-  int group, ctile;
-  if (!map_block(sh, group, ctile)) return;
+    ScanShape sh, const int32_t* __restrict__ chunk_cu, const int32_t* __restrict__ seq_cu,
+    SideArgs<T> ka, SideArgs<T> va) {
+  int side, group, ctile;
+  if (!map_block(sh, side, group, ctile)) return;
+  const SideArgs<T> a = side ? va : ka;
+  const T* __restrict__ x = a.x;
+  const T* __restrict__ dt = a.dt;
+  const T* __restrict__ bm = a.bm;
+  const T* __restrict__ cm = a.cm;
+  T* __restrict__ y = a.y;
   const int lane = threadIdx.x;
   const int c = ctile * kWave + lane;
   const int d = sh.d;
   const int q0 = group * kChunksPerWave;
   const int q1 = min(q0 + kChunksPerWave, sh.n_chunks);
 
-  SsmLane<T, N> sk, sv;
-  sk.load_params(A_k, D_k, bias_k, c);
-  sv.load_params(A_v, D_v, bias_v, c);
+  SsmLane<T, N> s;
+  s.load_params(a.A, a.D, a.bias, c);
 
   // end of chunk q: boundary state and, for the last chunk of a sequence, the hand-off state
-  auto chunk_end = [&](int q, int cs, int ce, float ok, float ov) {
-    if (kb) {
-      kb[q * d + c] = from_f32<T>(ok);
-      vb[q * d + c] = from_f32<T>(ov);
-    }
-    if (h_last_k) {
+  auto chunk_end = [&](int q, int cs, int ce, float out) {
+    if (a.b) a.b[q * d + c] = from_f32<T>(out);
+    if (a.h_last) {
       int lo = 0, hi = sh.S;        // sequence s with seq_cu[s] <= cs < seq_cu[s + 1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (seq_cu[mid] <= cs) lo = mid; else hi = mid;
       }
       if (seq_cu[lo + 1] == ce) {
-        float* hk = h_last_k + (static_cast<size_t>(lo) * d + c) * N;
-        float* hv = h_last_v + (static_cast<size_t>(lo) * d + c) * N;
+        float* hp = a.h_last + (static_cast<size_t>(lo) * d + c) * N;
 #pragma unroll
-        for (int n = 0; n < N; ++n) { hk[n] = sk.h[n]; hv[n] = sv.h[n]; }
+        for (int n = 0; n < N; ++n) hp[n] = s.h[n];
       }
     }
   };
@@ -150,66 +181,64 @@ __global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
   int cs = chunk_cu[q0];
   for (int q = q0; q < q1; ++q) {
     const int ce = chunk_cu[q + 1];
-    float ok = 0.f, ov = 0.f;
+    float out = 0.f;
     if (ce - cs == PU) {
-      float xs[PU], xvs[PU], dks[PU], dvs[PU];
+      float xs[PU], dts[PU];
 #pragma unroll
       for (int j = 0; j < PU; ++j) {
         const int o = (cs + j) * d + c;
-        xs[j] = to_f32(x[o]); dks[j] = to_f32(dtk[o]); dvs[j] = to_f32(dtv[o]);
-        xvs[j] = SEPX ? to_f32(xv[o]) : xs[j];
+        xs[j] = to_f32(x[o]);
+        dts[j] = to_f32(dt[o]);
       }
+      typename SsmLane<T, N>::Rows rn, rc;
+      SsmLane<T, N>::load_rows(bm + cs * N, cm + cs * N, rn);
 #pragma unroll
       for (int j = 0; j < PU; ++j) {
         const int t = cs + j;
-        if (j == 0) {
-          ok = sk.template step<true>(xs[j], dks[j], bmk + t * N, cmk + t * N);
-          ov = sv.template step<true>(xvs[j], dvs[j], bmv + t * N, cmv + t * N);
-        } else {
-          ok = sk.template step<false>(xs[j], dks[j], bmk + t * N, cmk + t * N);
-          ov = sv.template step<false>(xvs[j], dvs[j], bmv + t * N, cmv + t * N);
-        }
-        yk[t * d + c] = from_f32<T>(ok);
-        yv[t * d + c] = from_f32<T>(ov);
+        rc = rn;
+        rows_ready(rc.b[0], rc.c[0]);
+        if (j + 1 < PU) SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rn);
+        order_point();
+        if (j == 0) out = s.template step<true>(xs[j], dts[j], rc);
+        else out = s.template step<false>(xs[j], dts[j], rc);
+        y[t * d + c] = from_f32<T>(out);
       }
     } else {
-      float nx = to_f32(x[cs * d + c]), ndk = to_f32(dtk[cs * d + c]), ndv = to_f32(dtv[cs * d + c]);
-      float nxv = SEPX ? to_f32(xv[cs * d + c]) : nx;
+      float nx = to_f32(x[cs * d + c]), ndt = to_f32(dt[cs * d + c]);
+      typename SsmLane<T, N>::Rows rn, rc;
+      SsmLane<T, N>::load_rows(bm + cs * N, cm + cs * N, rn);
       for (int t = cs; t < ce; ++t) {
-        const float xk_t = nx, xv_t = nxv, dk = ndk, dv = ndv;
+        const float xt = nx, dtt = ndt;
+        rc = rn;
+        rows_ready(rc.b[0], rc.c[0]);
         if (t + 1 < ce) {
           const int o = (t + 1) * d + c;
-          nx = to_f32(x[o]); ndk = to_f32(dtk[o]); ndv = to_f32(dtv[o]);
-          nxv = SEPX ? to_f32(xv[o]) : nx;
+          nx = to_f32(x[o]);
+          ndt = to_f32(dt[o]);
+          SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rn);
         }
-        if (t == cs) {
-          ok = sk.template step<true>(xk_t, dk, bmk + t * N, cmk + t * N);
-          ov = sv.template step<true>(xv_t, dv, bmv + t * N, cmv + t * N);
-        } else {
-          ok = sk.template step<false>(xk_t, dk, bmk + t * N, cmk + t * N);
-          ov = sv.template step<false>(xv_t, dv, bmv + t * N, cmv + t * N);
-        }
-        yk[t * d + c] = from_f32<T>(ok);
-        yv[t * d + c] = from_f32<T>(ov);
+        order_point();
+        if (t == cs) out = s.template step<true>(xt, dtt, rc);
+        else out = s.template step<false>(xt, dtt, rc);
+        y[t * d + c] = from_f32<T>(out);
       }
     }
-    chunk_end(q, cs, ce, ok, ov);
+    chunk_end(q, cs, ce, out);
     cs = ce;
   }
 }
 
-template <typename T, int N, bool SEPX>
+template <typename T, int N>
 hipError_t launch_typed(const attamba_scan_args& a, const ScanShape& sh, hipStream_t stream) {
-  const int blocks = ceil_div(sh.groups, 8) * 8 * sh.ctiles;
-  hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, SEPX>), dim3(blocks), dim3(kWave), 0, stream, sh,
-                     a.chunk_cu, static_cast<const T*>(a.x), static_cast<const T*>(a.x_v),
-                     static_cast<const T*>(a.dt_k),
-                     static_cast<const T*>(a.dt_v), static_cast<const T*>(a.bm_k),
-                     static_cast<const T*>(a.cm_k), static_cast<const T*>(a.bm_v),
-                     static_cast<const T*>(a.cm_v), a.A_k, a.A_v, a.D_k, a.D_v, a.bias_k,
-                     a.bias_v, static_cast<T*>(a.y_k), static_cast<T*>(a.y_v),
-                     static_cast<T*>(a.kb), static_cast<T*>(a.vb), a.seq_cu, a.h_last_k,
-                     a.h_last_v);
+  const int blocks = ceil_div(sh.groups, 8) * 8 * sh.ctiles * 2;
+  SideArgs<T> k{static_cast<const T*>(a.x), static_cast<const T*>(a.dt_k),
+                static_cast<const T*>(a.bm_k), static_cast<const T*>(a.cm_k), a.A_k, a.D_k,
+                a.bias_k, static_cast<T*>(a.y_k), static_cast<T*>(a.kb), a.h_last_k};
+  SideArgs<T> v{static_cast<const T*>(a.x_v ? a.x_v : a.x), static_cast<const T*>(a.dt_v),
+                static_cast<const T*>(a.bm_v), static_cast<const T*>(a.cm_v), a.A_v, a.D_v,
+                a.bias_v, static_cast<T*>(a.y_v), static_cast<T*>(a.vb), a.h_last_v};
+  hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8>), dim3(blocks), dim3(kWave), 0, stream, sh,
+                     a.chunk_cu, a.seq_cu, k, v);
   return hipGetLastError();
 }
 
@@ -221,13 +250,9 @@ hipError_t launch_kvssm_scan(const attamba_scan_args& a, hipStream_t stream) {
   sh.T = a.T; sh.d = a.d; sh.n_chunks = a.n_chunks; sh.S = a.S;
   sh.groups = ceil_div(a.n_chunks, kChunksPerWave);
   sh.ctiles = a.d / kWave;
-  const bool sep = a.x_v != nullptr && a.x_v != a.x;
-  if (a.dtype == ATTAMBA_BF16) {
-    if (sep) return a.N == 16 ? launch_typed<__bf16, 16, true>(a, sh, stream) : launch_typed<__bf16, 32, true>(a, sh, stream);
-    return a.N == 16 ? launch_typed<__bf16, 16, false>(a, sh, stream) : launch_typed<__bf16, 32, false>(a, sh, stream);
-  }
-  if (sep) return a.N == 16 ? launch_typed<float, 16, true>(a, sh, stream) : launch_typed<float, 32, true>(a, sh, stream);
-  return a.N == 16 ? launch_typed<float, 16, false>(a, sh, stream) : launch_typed<float, 32, false>(a, sh, stream);
+  if (a.dtype == ATTAMBA_BF16)
+    return a.N == 16 ? launch_typed<__bf16, 16>(a, sh, stream) : launch_typed<__bf16, 32>(a, sh, stream);
+  return a.N == 16 ? launch_typed<float, 16>(a, sh, stream) : launch_typed<float, 32>(a, sh, stream);
 }
 
 }  // namespace attamba
