@@ -3,7 +3,9 @@
 A step is one pass of the whole hot path over one batch of synthetic input already resident
 in HBM: chunk segmentation, the fused SSM_K/SSM_V scan, and the chunk-aware attention. The
 default workload is the prefill configuration (bf16, B=2, n=8192, d=2048, 32 heads x 64,
-N=16, P=8, L=64, uniform chunks, M_test + window). Prints one JSON line.
+N=16, P=8, L=64, uniform chunks, M_test + window). Prints one JSON line. Its value is the hot
+back-to-back rate; the line also carries per-step times with the caches flushed first (the
+train_bf16 forward's working set fits in the 256 MB MALL, so both are reported).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload prefill_bf16|varchunk_bf16|train_bf16]
     python bench.py --workload decode_bf16      # decode configuration, separate line
@@ -59,14 +61,14 @@ def source_sha(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, sources) -> dict | None:
+def measured_traffic(kernel: str, sources, workload: str) -> dict | None:
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
-    the current kernel source."""
+    the current kernel source and on this workload (the bytes depend on the shapes)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha") != source_sha(*sources):
+    if rec.get("source_sha") != source_sha(*sources) or rec.get("workload") != workload:
         return None
     return rec
 
@@ -220,6 +222,20 @@ def bench_prefill(args):
     seg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    # the same steps with the caches flushed before each one (a 512 MiB write evicts the L2s and
+    # the 256 MB MALL, which can otherwise hold a small configuration's whole working set)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for k, e in enumerate(evf):
+        flush_buf.fill_(k & 0xFF)
+        step(e)
+    torch.cuda.synchronize()
+    del flush_buf
+    flushed = {"kernels_us": {"segmentation": round(float(np.mean([e[0].elapsed_time(e[1]) for e in evf])) * 1e3, 2),
+                              "kvssm_scan": round(float(np.mean([e[1].elapsed_time(e[2]) for e in evf])) * 1e3, 2),
+                              "chunk_attn": round(float(np.mean([e[2].elapsed_time(e[3]) for e in evf])) * 1e3, 2)},
+               "step_us": round(float(np.mean([e[0].elapsed_time(e[3]) for e in evf])) * 1e3, 2),
+               "note": "HIP events around each step after a 512 MiB device write; value and kernels_us are hot"}
 
     ms = wall * 1e3 / args.steps
     tok_s = T / (wall / args.steps)
@@ -233,9 +249,9 @@ def bench_prefill(args):
     scan_slots = SLOTS_PER_UPDATE * updates
     scan_alu_tslots = scan_slots / (scan_ms * 1e-3) / 1e12
     alu_peak = VALU_SLOTS_PER_S / 1e12
-    traffic = measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"])
+    traffic = measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"], args.workload)
     attn_traffic = measured_traffic("attn_mfma_kernel", ["attn_mfma.hip", "attn_geom.h", "attn_tiles.h",
-                                                         "common.h"])
+                                                         "common.h"], args.workload)
     roofline = {"bound": "alu", "kernel": "kvssm_scan_kernel", "achieved": round(scan_alu_tslots, 3),
                 "peak": round(alu_peak, 3), "unit": "T VALU-slot/s", "frac": round(scan_alu_tslots / alu_peak, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
@@ -253,6 +269,7 @@ def bench_prefill(args):
         "roofline": roofline,
         "kernels_us": {"segmentation": round(seg_ms * 1e3, 2), "kvssm_scan": round(scan_ms * 1e3, 2),
                        "chunk_attn": round(attn_ms * 1e3, 2)},
+        "flushed": flushed,
         "scan_hbm": {"algorithmic_bytes": scan_bytes, "GBps": round(scan_gbps, 1),
                      "frac_of_8TBps": round(scan_gbps / HBM_PEAK_GBPS, 4)},
         "attn_mfma": {"algorithmic_flop": attn_flop, "visible_pairs_per_head": pairs,
@@ -310,7 +327,7 @@ def bench_decode(args):
     kv_bytes = keys * cfg.B * cfg.H * cfg.hd * 2 * e
     state_bytes = cfg.steps * 2 * 2 * cfg.B * cfg.d * cfg.N * 4
     gbps = (kv_bytes + state_bytes) / wall / 1e9
-    traffic = measured_traffic("decode_step", ["decode.hip", "common.h"])
+    traffic = measured_traffic("decode_step", ["decode.hip", "common.h"], args.workload)
     line = {"metric": "decode tokens/s (boundary-state cache)", "value": round(cfg.B * cfg.steps / wall, 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": cfg.steps, "warmup": args.warmup,
             "ms_per_step": round(wall * 1e3 / cfg.steps, 4), "higher_is_better": True,
@@ -356,7 +373,7 @@ def bench_proj(args):
     n_out = sum(inp.widths)
     flop = 2.0 * T * d * n_out
     tflops = flop / (us * 1e-6) / 1e12
-    traffic = measured_traffic("proj_gemm_kernel", ["proj_gemm.hip", "common.h"])
+    traffic = measured_traffic("proj_gemm_kernel", ["proj_gemm.hip", "common.h"], args.workload)
     print(json.dumps({
         "metric": "input projections TFLOP/s (x W^T, bf16)", "value": round(tflops, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -546,7 +563,7 @@ def bench_train(args):
     updates = 2 * T * d * N
     alu_peak = VALU_SLOTS_PER_S / 1e12
     ach = SLOTS_PER_UPDATE_BWD * updates / (sbwd_ms * 1e-3) / 1e12
-    traffic = measured_traffic("kvssm_scan_bwd_kernel", ["kvssm_scan_bwd.hip", "common.h"])
+    traffic = measured_traffic("kvssm_scan_bwd_kernel", ["kvssm_scan_bwd.hip", "common.h"], args.workload)
     line = {
         "metric": "tokens/sec, KV-SSM forward + backward (training step)",
         "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,

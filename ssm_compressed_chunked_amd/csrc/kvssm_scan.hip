@@ -16,11 +16,12 @@
 // kernel.
 // One SSM per wave (rather than both) halves the scalar registers a token's rows need, which
 // leaves room to request the next token's rows before the current token's arithmetic, and
-// halves the vector registers per lane (about 70: 7 waves per SIMD to hide latency).
+// halves the vector registers per lane (72: 7 waves per SIMD to hide latency).
 // Chunks of the common length PU are processed fully unrolled: all x/dt loads of the chunk are
 // issued at its start, and no state value is carried across a loop back-edge (it restarts at
 // the next chunk anyway), so no register copies are needed. Other chunk lengths (random
-// chunking, a partial first or last chunk) take a token loop with the same one-token prefetch.
+// chunking, a partial first or last chunk) run in blocks of up to PU tokens with the same
+// loads up front and the same one-token row prefetch.
 #include "common.h"
 #include "kernels.h"
 
@@ -141,7 +142,9 @@ __device__ __forceinline__ void rows_ready(uint32_t b0, uint32_t c0) {
 }
 
 template <typename T, int N, int PU>
-__global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
+// bf16 with N = 16 (the common case) is held to 7 waves per SIMD (72 VGPRs; the other-length
+// path would otherwise take 73 and lose a wave); the other instances are left unconstrained.
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 && sizeof(T) == 2 ? 7 : 1))) void kvssm_scan_kernel(
     ScanShape sh, const int32_t* __restrict__ chunk_cu, const int32_t* __restrict__ seq_cu,
     SideArgs<T> ka, SideArgs<T> va) {
   int side, group, ctile;
@@ -204,23 +207,32 @@ __global__ __launch_bounds__(kWave) void kvssm_scan_kernel(
         y[t * d + c] = from_f32<T>(out);
       }
     } else {
-      float nx = to_f32(x[cs * d + c]), ndt = to_f32(dt[cs * d + c]);
-      typename SsmLane<T, N>::Rows rn, rc;
-      SsmLane<T, N>::load_rows(bm + cs * N, cm + cs * N, rn);
-      for (int t = cs; t < ce; ++t) {
-        const float xt = nx, dtt = ndt;
-        rc = rn;
-        rows_ready(rc.b[0], rc.c[0]);
-        if (t + 1 < ce) {
-          const int o = (t + 1) * d + c;
-          nx = to_f32(x[o]);
-          ndt = to_f32(dt[o]);
-          SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rn);
+      // any other length: blocks of up to PU tokens, each with its x/dt loads issued up front
+      // (the state runs on across the blocks of a chunk)
+      for (int bs = cs; bs < ce; bs += PU) {
+        const int nb = min(PU, ce - bs);
+        float xs[PU], dts[PU];
+#pragma unroll
+        for (int j = 0; j < PU; ++j) {   // past the block's end: its last token again (unused)
+          const int o = (bs + min(j, nb - 1)) * d + c;
+          xs[j] = to_f32(x[o]);
+          dts[j] = to_f32(dt[o]);
         }
-        order_point();
-        if (t == cs) out = s.template step<true>(xt, dtt, rc);
-        else out = s.template step<false>(xt, dtt, rc);
-        y[t * d + c] = from_f32<T>(out);
+        typename SsmLane<T, N>::Rows rn, rc;
+        SsmLane<T, N>::load_rows(bm + bs * N, cm + bs * N, rn);
+#pragma unroll
+        for (int j = 0; j < PU; ++j) {
+          if (j < nb) {
+            const int t = bs + j;
+            rc = rn;
+            rows_ready(rc.b[0], rc.c[0]);
+            if (j + 1 < nb) SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rn);
+            order_point();
+            if (j == 0 && bs == cs) out = s.template step<true>(xs[j], dts[j], rc);
+            else out = s.template step<false>(xs[j], dts[j], rc);
+            y[t * d + c] = from_f32<T>(out);
+          }
+        }
       }
     }
     chunk_end(q, cs, ce, out);
