@@ -22,14 +22,16 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(z) = ln(1 + e^z). ln(1 + e) is taken as ln(w) * e / (w - 1) with w = 1 + e, which
-// keeps full relative accuracy when e is small (D. Goldberg, "What every computer scientist
-// should know about floating-point arithmetic", 1991, Theorem 4); for z > 20 the result is z
-// to float32 precision.
+// softplus(z) = ln(1 + e^z) with e = e^z and w = fl(1 + e). For e < 1 the rounding error of that
+// sum, c = e - (w - 1), is exact (Dekker's Fast2Sum: |1| >= |e|, and w - 1 is exact by Sterbenz's
+// lemma), and ln(1 + e) = ln(w) + ln(1 + c / w) = ln(w) + c to within c e, which keeps full
+// relative accuracy when e is small. For e >= 1 the correction (at most 2^-24) is about one ulp
+// of the result or less and is left out; for z > 20 the result is z to float32 precision.
 __device__ __forceinline__ float softplus_f32(float z) {
   const float e = hw_exp2(z * kLog2e);
   const float w = 1.0f + e;
-  const float r = (w == 1.0f) ? e : (hw_log2(w) * kLn2) * (e * hw_rcp(w - 1.0f));
+  const float c = e < 1.0f ? e - (w - 1.0f) : 0.0f;
+  const float r = fmaf(hw_log2(w), kLn2, c);
   return z > 20.0f ? z : r;
 }
 
