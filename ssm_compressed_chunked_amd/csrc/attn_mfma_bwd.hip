@@ -21,6 +21,8 @@
 // boundary states first, then the band), with per tile
 //   S^T = K Q^T,  dP^T = V dO^T  (Q and dO in registers),  dS^T = P^T (dP^T - D),
 //   dQ^T (hd x queries) += K^T dS^T   (K^T through the transposing LDS read).
+// It runs first and also writes D_i = dO_i . O_i and every row's w_i and c0 + E_i (the row
+// geometry the dK/dV kernel searches), so the backward is two launches.
 #include "common.h"
 #include "attn_geom.h"
 #include "attn_tiles.h"
@@ -344,21 +346,38 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_mfma_kernel(AttnBwdParams bp) 
   const int topb = c0 + gl.E - 1;
 
   bf16x8 qf[QS], gf8[QS];
+  float Dl;   // D_i = dO_i . O_i (this lane's half of the row, then both halves)
   {
     const size_t ro = static_cast<size_t>(ic) * hs + h * HD + 8 * hf;
     const __bf16* qr = static_cast<const __bf16*>(p.q) + ro;
     const __bf16* gr = static_cast<const __bf16*>(bp.dout) + ro;
+    const __bf16* orow = static_cast<const __bf16*>(p.out) + ro;
+    float part = 0.f;
 #pragma unroll
     for (int st = 0; st < QS; ++st) {
       qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
       gf8[st] = *reinterpret_cast<const bf16x8*>(gr + 16 * st);
+      const bf16x8 of = *reinterpret_cast<const bf16x8*>(orow + 16 * st);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 a = {of[e], of[e + 1]}, b = {gf8[st][e], gf8[st][e + 1]};
+        part = __builtin_amdgcn_fdot2_f32_bf16(a, b, part, false);
+      }
     }
+    Dl = half_sum(part);
   }
-  float lse2 = INFINITY, Dl = 0.f;
+  float lse2 = INFINITY;
   if (i < s1) {
     const float ls = p.lse[static_cast<size_t>(h) * p.T + i];
     if (ls != -INFINITY) lse2 = ls * kLog2e;
-    Dl = bp.delta[static_cast<size_t>(h) * p.T + i];
+    // D_i and the row's mask geometry for the dK/dV kernel, which runs after this one
+    if (hf == 0) {
+      bp.delta[static_cast<size_t>(h) * p.T + i] = Dl;
+      if (h == 0) {
+        bp.row_w[i] = g.w;
+        bp.row_ce[i] = c0 + g.E;
+      }
+    }
   }
   f32x16 dqa[OB];
 #pragma unroll
@@ -475,12 +494,13 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, int hd, hipStream_t stre
   const int n_bh8 = ceil_div(p.f.S * p.f.H, 8) * 8;
   const dim3 gkv(2 * ceil_div(p.f.max_seqlen, BK) * n_bh8);
   const dim3 gq(ceil_div(p.f.max_seqlen, 128) * n_bh8);
+  // dQ first: it also writes D_i = dO_i . O_i and every row's w_i and c0 + E_i, which dK/dV reads
   if (hd == 64) {
-    hipLaunchKernelGGL(attn_bwd_dkv_mfma_kernel<64>, gkv, dim3(NT), 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel<64>, gq, dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dkv_mfma_kernel<64>, gkv, dim3(NT), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(attn_bwd_dkv_mfma_kernel<128>, gkv, dim3(NT), 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel<128>, gq, dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dkv_mfma_kernel<128>, gkv, dim3(NT), 0, stream, p);
   }
   return hipGetLastError();
 }

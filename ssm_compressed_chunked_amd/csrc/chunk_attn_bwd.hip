@@ -15,8 +15,8 @@
 // rows that see a key form one contiguous range, because w_i and E_i grow with i, found by
 // binary search; the lanes of a wave walk the union of their ranges in step, so every row is
 // read once per wave as a broadcast). bf16 with head dims 64 and 128 goes to the matrix-core
-// kernels (attn_mfma_bwd.hip) after the row-sum and row-geometry kernels here; these generic
-// kernels cover float32 and head dim 32.
+// kernels (attn_mfma_bwd.hip, whose dQ kernel computes D itself); these generic kernels cover
+// float32 and head dim 32.
 #include "attn_geom.h"
 #include "common.h"
 
@@ -34,19 +34,6 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(AttnBwdParams p) {
 #pragma unroll 8
   for (int e = 0; e < HD; ++e) acc = fmaf(to_f32(o[e]), to_f32(g[e]), acc);
   p.delta[static_cast<size_t>(h) * p.f.T + i] = acc;
-}
-
-// Per-row mask geometry (w_i and c0 + E_i), for the matrix-core kernels' row ranges and masks.
-__global__ __launch_bounds__(256) void attn_bwd_rows_kernel(AttnBwdParams bp) {
-  const AttnParams& p = bp.f;
-  const int s = blockIdx.y;
-  const int s0 = p.seq_cu[s], s1 = p.seq_cu[s + 1];
-  const int i = s0 + blockIdx.x * 256 + threadIdx.x;
-  if (i >= s1) return;
-  const int c0 = p.token_chunk[s0];
-  const RowGeom g = row_geom(p, i, s0, s1, c0);
-  bp.row_w[i] = g.w;
-  bp.row_ce[i] = c0 + g.E;
 }
 
 template <typename T, int HD>
@@ -209,18 +196,7 @@ hipError_t launch_generic(const AttnBwdParams& p, hipStream_t stream) {
 
 hipError_t launch_chunk_attn_bwd(const AttnBwdParams& p, int hd, int dtype, hipStream_t stream) {
   if (p.f.T == 0) return hipSuccess;
-  if (dtype == ATTAMBA_BF16 && (hd == 64 || hd == 128)) {
-    const AttnParams& f = p.f;
-    if (hd == 64)
-      hipLaunchKernelGGL((attn_bwd_delta_kernel<__bf16, 64>), dim3(ceil_div(f.T * f.H, 256)), dim3(256), 0,
-                         stream, p);
-    else
-      hipLaunchKernelGGL((attn_bwd_delta_kernel<__bf16, 128>), dim3(ceil_div(f.T * f.H, 256)), dim3(256), 0,
-                         stream, p);
-    hipLaunchKernelGGL(attn_bwd_rows_kernel, dim3(ceil_div(f.max_seqlen, 256), f.S), dim3(256), 0, stream, p);
-    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    return launch_attn_bwd_mfma(p, hd, stream);
-  }
+  if (dtype == ATTAMBA_BF16 && (hd == 64 || hd == 128)) return launch_attn_bwd_mfma(p, hd, stream);
   if (dtype == ATTAMBA_BF16) {
     if (hd == 32) return launch_generic<__bf16, 32>(p, stream);
     if (hd == 64) return launch_generic<__bf16, 64>(p, stream);
