@@ -28,11 +28,15 @@
 namespace attamba {
 namespace {
 
-constexpr int kChunksPerWave = 2;
+// Waves the chip holds at once at this kernel's occupancy (256 CUs x 4 SIMDs x 7 waves). A wave
+// walks two chunks (CPW = 2) when the grid then still spans at least 9 such rounds; otherwise
+// one, so that smaller grids end with a shorter last round.
+constexpr int kResidentWaves = 256 * 4 * 7;
+constexpr int kRoundsForTwoChunks = 9;
 
 struct ScanShape {
   int T, d, n_chunks, S;
-  int groups;          // chunk groups = ceil(n_chunks / kChunksPerWave)
+  int groups;          // chunk groups = ceil(n_chunks / chunks per wave)
   int ctiles;          // channel tiles = d / 64
 };
 
@@ -141,7 +145,7 @@ __device__ __forceinline__ void rows_ready(uint32_t b0, uint32_t c0) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename T, int N, int PU>
+template <typename T, int N, int PU, int CPW>
 // bf16 with N = 16 (the common case) is held to 7 waves per SIMD (72 VGPRs; the other-length
 // path would otherwise take 73 and lose a wave); the other instances are left unconstrained.
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 && sizeof(T) == 2 ? 7 : 1))) void kvssm_scan_kernel(
@@ -158,8 +162,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
   const int lane = threadIdx.x;
   const int c = ctile * kWave + lane;
   const int d = sh.d;
-  const int q0 = group * kChunksPerWave;
-  const int q1 = min(q0 + kChunksPerWave, sh.n_chunks);
+  const int q0 = group * CPW;
+  const int q1 = min(q0 + CPW, sh.n_chunks);
 
   SsmLane<T, N> s;
   s.load_params(a.A, a.D, a.bias, c);
@@ -241,7 +245,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
 }
 
 template <typename T, int N>
-hipError_t launch_typed(const attamba_scan_args& a, const ScanShape& sh, hipStream_t stream) {
+hipError_t launch_typed(const attamba_scan_args& a, const ScanShape& sh, int cpw,
+                        hipStream_t stream) {
   const int blocks = ceil_div(sh.groups, 8) * 8 * sh.ctiles * 2;
   SideArgs<T> k{static_cast<const T*>(a.x), static_cast<const T*>(a.dt_k),
                 static_cast<const T*>(a.bm_k), static_cast<const T*>(a.cm_k), a.A_k, a.D_k,
@@ -249,8 +254,12 @@ hipError_t launch_typed(const attamba_scan_args& a, const ScanShape& sh, hipStre
   SideArgs<T> v{static_cast<const T*>(a.x_v ? a.x_v : a.x), static_cast<const T*>(a.dt_v),
                 static_cast<const T*>(a.bm_v), static_cast<const T*>(a.cm_v), a.A_v, a.D_v,
                 a.bias_v, static_cast<T*>(a.y_v), static_cast<T*>(a.vb), a.h_last_v};
-  hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8>), dim3(blocks), dim3(kWave), 0, stream, sh,
-                     a.chunk_cu, a.seq_cu, k, v);
+  if (cpw == 2)
+    hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, 2>), dim3(blocks), dim3(kWave), 0, stream, sh,
+                       a.chunk_cu, a.seq_cu, k, v);
+  else
+    hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, 1>), dim3(blocks), dim3(kWave), 0, stream, sh,
+                       a.chunk_cu, a.seq_cu, k, v);
   return hipGetLastError();
 }
 
@@ -260,11 +269,13 @@ hipError_t launch_kvssm_scan(const attamba_scan_args& a, hipStream_t stream) {
   if (a.n_chunks == 0 || a.T == 0) return hipSuccess;
   ScanShape sh;
   sh.T = a.T; sh.d = a.d; sh.n_chunks = a.n_chunks; sh.S = a.S;
-  sh.groups = ceil_div(a.n_chunks, kChunksPerWave);
   sh.ctiles = a.d / kWave;
+  const long waves2 = static_cast<long>(ceil_div(ceil_div(a.n_chunks, 2), 8)) * 8 * sh.ctiles * 2;
+  const int cpw = waves2 >= static_cast<long>(kRoundsForTwoChunks) * kResidentWaves ? 2 : 1;
+  sh.groups = ceil_div(a.n_chunks, cpw);
   if (a.dtype == ATTAMBA_BF16)
-    return a.N == 16 ? launch_typed<__bf16, 16>(a, sh, stream) : launch_typed<__bf16, 32>(a, sh, stream);
-  return a.N == 16 ? launch_typed<float, 16>(a, sh, stream) : launch_typed<float, 32>(a, sh, stream);
+    return a.N == 16 ? launch_typed<__bf16, 16>(a, sh, cpw, stream) : launch_typed<__bf16, 32>(a, sh, cpw, stream);
+  return a.N == 16 ? launch_typed<float, 16>(a, sh, cpw, stream) : launch_typed<float, 32>(a, sh, cpw, stream);
 }
 
 }  // namespace attamba
