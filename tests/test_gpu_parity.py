@@ -245,6 +245,46 @@ def test_full_size_sampled(cfg):
     check_close(res["lse"][:, rows].cpu().numpy(), lse, cfg.dtype, "lse rows")
 
 
+@pytest.mark.parametrize("cfg", [PREFILL_BF16, VARCHUNK_BF16], ids=lambda c: c.name)
+def test_full_size_handoff_and_boundaries(cfg):
+    """At full size (prefill_bf16's grid walks two chunks per wave, varchunk_bf16's one, with
+    chunks of up to 16 tokens in two blocks): every sequence's hand-off state against the oracle
+    run over that sequence's last chunk alone (the state restarts at every chunk start, so the
+    last chunk fixes it), and every boundary state equal to the per-token output at its chunk's
+    last token (the same value, stored twice)."""
+    say(f"full-size hand-off {cfg.name}")
+    inp = make_prefill(cfg)
+    act, par = to_dev(inp)
+    rnd = cfg.chunking == "random"
+    P = None if rnd else cfg.P
+    seq_cu = torch.from_numpy(inp.seq_cu).cuda()
+    T = cfg.T
+    lay = chunk_layout(inp.seq_cu, seq_cu, T, P, cfg.layer_idx, chunk_lens=inp.chunk_lens)
+    s = att.kvssm_scan(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"], act["bm_v"],
+                       act["cm_v"], par["A_k"], par["A_v"], par["D_k"], par["D_v"], par["bias_k"],
+                       par["bias_v"], lay.chunk_cu, seq_cu=seq_cu, h_last=True)
+    torch.cuda.synchronize()
+    ref_cu = oracle.segment(inp.seq_cu, P, cfg.layer_idx, inp.chunk_lens)[0]
+    ends = ref_cu[1:] - 1
+    for tag in ("k", "v"):
+        y, kb = s[f"y_{tag}"], s[f"{tag}b"]
+        assert torch.equal(kb, y[torch.from_numpy(ends.astype(np.int64)).cuda()]), f"{tag}b != y at chunk ends"
+    f = f64_inputs(inp)
+    got = {tag: s[f"h_last_{tag}"].cpu().numpy() for tag in ("k", "v")}
+    for si in range(len(inp.seq_cu) - 1):
+        e = int(inp.seq_cu[si + 1]) - 1
+        q = int(np.searchsorted(ref_cu, e, side="right")) - 1     # the sequence's last chunk
+        a = int(ref_cu[q])
+        for tag in ("k", "v"):
+            _, snaps = oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
+                                             f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"], ref_cu,
+                                             t_begin=a, t_end=e + 1, snapshot_after={e})
+            ref = snaps[e]
+            # the state is float32 on the GPU from bf16 inputs: 1e-3 relative to its scale
+            assert np.abs(got[tag][si] - ref).max() <= 1e-3 * (np.abs(ref).max() + 1e-6), \
+                f"h_last_{tag} of sequence {si}"
+
+
 # ------------------------------------------------------------------------------ decode
 @pytest.mark.parametrize("H,hd,N,P,L,layer,n0,steps,dtype", [
     (2, 128, 16, 4, 8, 0, 21, 13, "bf16"),
