@@ -617,9 +617,9 @@ def att_ends_before(x, P, o):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by batch, head or sequence with no exchange beyond one "
-              "all-gather of boundary states; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would "
+              "shard by batch, head or sequence, with no exchange beyond one all-gather of the "
+              "boundary states and a halo of the last L keys)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
