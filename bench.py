@@ -521,7 +521,8 @@ def bench_train(args):
     dout_h = make_output_grad((T, H, hd), cfg.dtype, seed=42)
     dout = dout_h.cuda()
     stream = torch.cuda.current_stream()
-    ws = torch.empty((H + 2, T), dtype=torch.float32, device="cuda")
+    ws = att.chunk_attn_bwd_workspace(T, H, hd, att.count_chunks(inp.seq_cu, cfg.P, cfg.layer_idx),
+                                      act["q"].dtype)
 
     def step(ev=None):
         if ev is not None:

@@ -329,7 +329,8 @@ int attamba_input_proj(const attamba_proj_args* args, attamba_stream_t stream);
  *   it), to dk/dv. The total gradient of the per-token SSM output at a chunk's last token is
  *   dk plus that chunk's dkb (attamba_kvssm_scan_bwd adds them when given gkb/gvb).
  * All gradients are written in fwd.dtype; every element of dq, dk, dv, dkb, dvb is written.
- * Errors: as attamba_chunk_attn_fwd, plus NULL_ARG for lse, dout, a gradient or workspace. */
+ * Errors: as attamba_chunk_attn_fwd, plus NULL_ARG for lse, dout, a gradient or workspace, and
+ * CAPACITY when workspace_elems is below attamba_chunk_attn_bwd_workspace_size(). */
 typedef struct {
   attamba_attn_args fwd;
   const void* dout;    /* [T, H, hd] gradient of out */
@@ -338,10 +339,18 @@ typedef struct {
   void* dv;            /* [T, H, hd] out: gradient of v */
   void* dkb;           /* [n_chunks, H, hd] out: gradient of kb */
   void* dvb;           /* [n_chunks, H, hd] out: gradient of vb */
-  float* workspace;    /* device scratch of (H + 2) * T 4-byte elements */
+  float* workspace;    /* device scratch, caller-owned, contents on entry ignored */
+  size_t workspace_elems; /* its size in 4-byte elements */
 } attamba_attn_bwd_args;
 
 int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* args, attamba_stream_t stream);
+
+/* 4-byte workspace elements attamba_chunk_attn_bwd needs for these arguments (only fwd.T, H,
+ * hd, n_chunks and dtype are read): (H + 2) * T; for bf16 with hd 64 or 128 and at least 4
+ * tokens per chunk, that rounded up to a multiple of 64, plus 8 * n_chunks * H * hd (float32
+ * partial sums of the dK/dV of the boundary states, whose query rows are split over 4
+ * workgroups). The workspace must be 16-byte aligned. Errors: NULL_ARG, BAD_SHAPE. */
+int attamba_chunk_attn_bwd_workspace_size(const attamba_attn_bwd_args* args, size_t* elems);
 
 /* KV-SSM scan backward. fwd holds the forward call's arguments (only its inputs are read; its
  * outputs may be NULL). Given the gradients of y_k, y_v (and optionally of kb, vb, added at each

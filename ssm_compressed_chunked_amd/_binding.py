@@ -60,7 +60,7 @@ class DecodePrefixStruct(C.Structure):
 
 class AttnBwdArgs(C.Structure):
     _fields_ = [("fwd", AttnArgs), ("dout", _vp), ("dq", _vp), ("dk", _vp), ("dv", _vp),
-                ("dkb", _vp), ("dvb", _vp), ("workspace", _vp)]
+                ("dkb", _vp), ("dvb", _vp), ("workspace", _vp), ("workspace_elems", C.c_size_t)]
 
 
 class ScanBwdArgs(C.Structure):
@@ -102,6 +102,7 @@ EXPORTS = {
     "attamba_decode_load_prefix": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodePrefixStruct), _vp],
                                    C.c_int),
     "attamba_chunk_attn_bwd": ([C.POINTER(AttnBwdArgs), _vp], C.c_int),
+    "attamba_chunk_attn_bwd_workspace_size": ([C.POINTER(AttnBwdArgs), C.POINTER(C.c_size_t)], C.c_int),
     "attamba_kvssm_scan_bwd": ([C.POINTER(ScanBwdArgs), _vp], C.c_int),
 }
 
@@ -374,6 +375,17 @@ def chunk_attn_fwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: i
     return out, lse
 
 
+def chunk_attn_bwd_workspace(T: int, H: int, hd: int, n_chunks: int, dtype, device="cuda"):
+    """A workspace for chunk_attn_bwd at these sizes (float32, sized by the library; allocate
+    once and pass it to every call of that shape)."""
+    b = AttnBwdArgs()
+    b.fwd.T, b.fwd.H, b.fwd.hd, b.fwd.n_chunks = T, H, hd, n_chunks
+    b.fwd.dtype = BF16 if dtype == torch.bfloat16 else FP32
+    need = C.c_size_t(0)
+    _check(lib().attamba_chunk_attn_bwd_workspace_size(C.byref(b), C.byref(need)))
+    return torch.empty(max(need.value, 1), dtype=torch.float32, device=device)
+
+
 def chunk_attn_bwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: int, L: int,
                    mode: int, out, lse, dout, scale: float = 0.0, workspace=None,
                    stream=None) -> dict:
@@ -389,9 +401,12 @@ def chunk_attn_bwd(q, k, v, kb, vb, seq_cu, chunk_cu, token_chunk, max_seqlen: i
     b.fwd.out = _dev(out, "out", act, T * H * hd)
     b.fwd.lse = _dev(lse, "lse", torch.float32, H * T)
     b.dout = _dev(dout, "dout", act, T * H * hd)
+    need = C.c_size_t(0)
+    _check(lib().attamba_chunk_attn_bwd_workspace_size(C.byref(b), C.byref(need)))
     if workspace is None:
-        workspace = torch.empty((H + 2, T), dtype=torch.float32, device=q.device)
-    b.workspace = _dev(workspace, "workspace", torch.float32, (H + 2) * T)
+        workspace = torch.empty(max(need.value, 1), dtype=torch.float32, device=q.device)
+    b.workspace = _dev(workspace, "workspace", torch.float32)
+    b.workspace_elems = workspace.numel()
     g = dict(dq=torch.empty_like(q), dk=torch.empty_like(q), dv=torch.empty_like(q),
              dkb=torch.empty((n_chunks, H, hd), dtype=act, device=q.device),
              dvb=torch.empty((n_chunks, H, hd), dtype=act, device=q.device))

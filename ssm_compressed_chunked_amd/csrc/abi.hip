@@ -232,6 +232,12 @@ int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* b, attamba_stream_t stre
   if (const int st = check_attn(a, "chunk_attn_bwd")) return st;
   if (a->T > 0 && (!a->lse || !b->dout || !b->dq || !b->dk || !b->dv || !b->dkb || !b->dvb || !b->workspace))
     return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_bwd: lse, dout, a gradient or the workspace is null");
+  if (a->T > 0 && reinterpret_cast<uintptr_t>(b->workspace) % 16 != 0)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_attn_bwd: the workspace must be 16-byte aligned");
+  const size_t need = attamba::attn_bwd_workspace_elems(a->T, a->H, a->hd, a->n_chunks, a->dtype);
+  if (b->workspace_elems < need)
+    return fail(ATTAMBA_ERR_CAPACITY, "chunk_attn_bwd: workspace of %zu elements, %zu needed",
+                b->workspace_elems, need);
   attamba::AttnBwdParams p{};
   attamba::AttnParams& f = p.f;
   f.T = a->T; f.H = a->H; f.S = a->S; f.max_seqlen = a->max_seqlen; f.L = a->L;
@@ -245,8 +251,24 @@ int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* b, attamba_stream_t stre
   p.row_w = reinterpret_cast<int*>(b->workspace + static_cast<size_t>(a->H) * a->T);
   p.row_ce = p.row_w + a->T;
   p.n_chunks = a->n_chunks;
+  p.dkv_split = attamba::attn_bwd_dkv_split(a->T, a->hd, a->n_chunks, a->dtype);
+  if (p.dkv_split > 1) {
+    const size_t part = static_cast<size_t>(p.dkv_split) * a->n_chunks * a->H * a->hd;
+    p.dkb_part = b->workspace + (static_cast<size_t>(a->H + 2) * a->T + 63) / 64 * 64;
+    p.dvb_part = p.dkb_part + part;
+  }
   return hip_status(attamba::launch_chunk_attn_bwd(p, a->hd, a->dtype, reinterpret_cast<hipStream_t>(stream)),
                     "chunk_attn_bwd launch");
+}
+
+int attamba_chunk_attn_bwd_workspace_size(const attamba_attn_bwd_args* b, size_t* elems) {
+  if (!b || !elems) return fail(ATTAMBA_ERR_NULL_ARG, "chunk_attn_bwd_workspace_size: null pointer");
+  const attamba_attn_args* a = &b->fwd;
+  if (a->T < 0 || a->H < 1 || a->n_chunks < 0)
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "chunk_attn_bwd_workspace_size: T=%d H=%d n_chunks=%d", a->T, a->H,
+                a->n_chunks);
+  *elems = attamba::attn_bwd_workspace_elems(a->T, a->H, a->hd, a->n_chunks, a->dtype);
+  return ATTAMBA_OK;
 }
 
 int attamba_input_proj(const attamba_proj_args* a, attamba_stream_t stream) {

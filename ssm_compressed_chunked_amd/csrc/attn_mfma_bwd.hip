@@ -22,7 +22,8 @@
 //   S^T = K Q^T,  dP^T = V dO^T  (Q and dO in registers),  dS^T = P^T (dP^T - D),
 //   dQ^T (hd x queries) += K^T dS^T   (K^T through the transposing LDS read).
 // It runs first and also writes D_i = dO_i . O_i and every row's w_i and c0 + E_i (the row
-// geometry the dK/dV kernel searches), so the backward is two launches.
+// geometry the dK/dV kernel searches). A third launch finalizes the boundary-state gradients
+// when their query rows were split over several dK/dV workgroups.
 #include "common.h"
 #include "attn_geom.h"
 #include "attn_tiles.h"
@@ -78,21 +79,27 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
   const AttnParams& p = bp.f;
 
   // Workgroups go round-robin to the 8 XCDs; all key tiles of one (sequence, head) sit on one
-  // XCD, boundary tiles (seen by the most rows) first.
-  const int n_kt = 2 * ceil_div(p.max_seqlen, BK);
+  // XCD, boundary tiles (seen by the most rows) first. A boundary tile is seen by every later
+  // row of its sequence, so its query rows are split over ns workgroups (parts), each walking a
+  // contiguous share of the query tiles; their float32 partial sums are added by a finalize
+  // launch. Per-token key tiles are seen by a few hundred rows and are not split.
+  const int ns = bp.dkv_split;
+  const int n_kt = (ns + 1) * ceil_div(p.max_seqlen, BK);
   const int id = blockIdx.x, slot = id >> 3;
   const int bh = (slot / n_kt) * 8 + (id & 7);
   if (bh >= p.S * p.H) return;
   const int s = bh / p.H, h = bh % p.H;
-  const int kt = slot % n_kt;
+  const int ks = slot % n_kt;
   const int s0 = p.seq_cu[s], s1 = p.seq_cu[s + 1];
   if (s1 <= s0) return;
   const int c0 = p.token_chunk[s0];
   const int nch = p.token_chunk[s1 - 1] + 1 - c0;
   const int nbt = ceil_div(nch, BK), nbd = ceil_div(s1 - s0, BK);
-  if (kt >= nbt + nbd) return;
-  const bool bnd = kt < nbt;
-  const int kbase = bnd ? c0 + kt * BK : s0 + (kt - nbt) * BK;
+  if (ks >= nbt * ns + nbd) return;
+  const bool bnd = ks < nbt * ns;
+  const int kt = bnd ? ks / ns : ks - nbt * ns;
+  const int part = bnd ? ks % ns : 0;
+  const int kbase = bnd ? c0 + kt * BK : s0 + kt * BK;
   const int ktop = bnd ? c0 + nch - 1 : s1 - 1;
   const int kmax = min(kbase + BK - 1, ktop);
   const int* __restrict__ row_w = bp.row_w;
@@ -121,6 +128,8 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
     }
   }
   const int nq = ib >= ia ? ceil_div(ib - ia + 1, BM) : 0;
+  const int nparts = bnd ? ns : 1;
+  const int tb = part * nq / nparts, te = (part + 1) * nq / nparts;   // this part's query tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -187,20 +196,20 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
     sm.wr[t & 1][lane] = m_w;
     sm.ce[t & 1][lane] = m_ce;
   };
-  if (nq > 0) {
-    issue(0);
+  if (te > tb) {
+    issue(tb);
     if (wid == 0) {
-      meta_load(0);
-      meta_store(0);
+      meta_load(tb);
+      meta_store(tb);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const float c = p.scale * kLog2e;
 
-  for (int t = 0; t < nq; ++t) {
+  for (int t = tb; t < te; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nq) {
+    if (t + 1 < te) {
       issue(t + 1);
       if (wid == 0) meta_load(t + 1);
     }
@@ -273,13 +282,27 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
           dka[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dk8[ks], dka[j], 0, 0, 0);
         }
     }
-    if (wid == 0 && t + 1 < nq) meta_store(t + 1);
+    if (wid == 0 && t + 1 < te) meta_store(t + 1);
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of tile t + 1 have landed ...
     __syncthreads();                   // ... and every wave is done with tile t
   }
 
   // epilogue: lane = key, accumulator rows = hd 32 j + 8 g + 4 hf + e
-  if (wave_live && kx <= ktop) {
+  if (wave_live && kx <= ktop && bnd && ns > 1) {
+    // this part's float32 partial sums (dK unscaled) into its slot [part][chunk][H * hd]
+    const size_t ro = (static_cast<size_t>(part) * bp.n_chunks + kx) * hs + h * HD + 4 * hf;
+    float* dkp = bp.dkb_part + ro;
+    float* dvp = bp.dvb_part + ro;
+#pragma unroll
+    for (int j = 0; j < OB; ++j)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 a = {dka[j][4 * g4], dka[j][4 * g4 + 1], dka[j][4 * g4 + 2], dka[j][4 * g4 + 3]};
+        const float4 b = {dva[j][4 * g4], dva[j][4 * g4 + 1], dva[j][4 * g4 + 2], dva[j][4 * g4 + 3]};
+        *reinterpret_cast<float4*>(dkp + 32 * j + 8 * g4) = a;
+        *reinterpret_cast<float4*>(dvp + 32 * j + 8 * g4) = b;
+      }
+  } else if (wave_live && kx <= ktop) {
     const size_t ro = static_cast<size_t>(kx) * hs + h * HD + 4 * hf;
     __bf16* dko = static_cast<__bf16*>(bnd ? bp.dkb : bp.dk) + ro;
     __bf16* dvo = static_cast<__bf16*>(bnd ? bp.dvb : bp.dv) + ro;
@@ -488,11 +511,44 @@ template __global__ void attn_bwd_dkv_mfma_kernel<128>(AttnBwdParams);
 template __global__ void attn_bwd_dq_mfma_kernel<64>(AttnBwdParams);
 template __global__ void attn_bwd_dq_mfma_kernel<128>(AttnBwdParams);
 
+// dkb = scale * (sum of the parts' dK), dvb = sum of the parts' dV, rounded to bf16; four
+// consecutive elements of [n_chunks, H * hd] per thread.
+__global__ __launch_bounds__(256) void attn_bwd_dkv_finalize_kernel(AttnBwdParams bp, int n) {
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 k = {0.f, 0.f, 0.f, 0.f}, v = {0.f, 0.f, 0.f, 0.f};
+  for (int part = 0; part < bp.dkv_split; ++part) {
+    const float4 a = *reinterpret_cast<const float4*>(bp.dkb_part + static_cast<size_t>(part) * n + i);
+    const float4 b = *reinterpret_cast<const float4*>(bp.dvb_part + static_cast<size_t>(part) * n + i);
+    k.x += a.x; k.y += a.y; k.z += a.z; k.w += a.w;
+    v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+  }
+  const float sc = bp.f.scale;
+  const bf16x4 ko = {static_cast<__bf16>(k.x * sc), static_cast<__bf16>(k.y * sc),
+                     static_cast<__bf16>(k.z * sc), static_cast<__bf16>(k.w * sc)};
+  const bf16x4 vo = {static_cast<__bf16>(v.x), static_cast<__bf16>(v.y), static_cast<__bf16>(v.z),
+                     static_cast<__bf16>(v.w)};
+  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(bp.dkb) + i) = ko;
+  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(bp.dvb) + i) = vo;
+}
+
 }  // namespace
+
+int attn_bwd_dkv_split(int T, int hd, int n_chunks, int dtype) {
+  const bool mfma = dtype == ATTAMBA_BF16 && (hd == 64 || hd == 128);
+  return mfma && static_cast<long>(n_chunks) * 4 <= T ? kDkvSplit : 1;
+}
+
+size_t attn_bwd_workspace_elems(int T, int H, int hd, int n_chunks, int dtype) {
+  size_t e = static_cast<size_t>(H + 2) * T;
+  const int ns = attn_bwd_dkv_split(T, hd, n_chunks, dtype);
+  if (ns > 1) e = (e + 63) / 64 * 64 + 2 * static_cast<size_t>(ns) * n_chunks * H * hd;
+  return e;
+}
 
 hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, int hd, hipStream_t stream) {
   const int n_bh8 = ceil_div(p.f.S * p.f.H, 8) * 8;
-  const dim3 gkv(2 * ceil_div(p.f.max_seqlen, BK) * n_bh8);
+  const dim3 gkv((p.dkv_split + 1) * ceil_div(p.f.max_seqlen, BK) * n_bh8);
   const dim3 gq(ceil_div(p.f.max_seqlen, 128) * n_bh8);
   // dQ first: it also writes D_i = dO_i . O_i and every row's w_i and c0 + E_i, which dK/dV reads
   if (hd == 64) {
@@ -501,6 +557,10 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, int hd, hipStream_t stre
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_mfma_kernel<128>, gq, dim3(NT), 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_dkv_mfma_kernel<128>, gkv, dim3(NT), 0, stream, p);
+  }
+  if (p.dkv_split > 1) {
+    const int n = p.n_chunks * p.f.H * hd;
+    hipLaunchKernelGGL(attn_bwd_dkv_finalize_kernel, dim3(ceil_div(n / 4, 256)), dim3(256), 0, stream, p, n);
   }
   return hipGetLastError();
 }

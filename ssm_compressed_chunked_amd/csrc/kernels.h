@@ -83,7 +83,18 @@ struct AttnBwdParams {
   int* row_w;                     // [T] first band position w_i of every row
   int* row_ce;                    // [T] c0 + E_i: first boundary state row i does not see
   int n_chunks;
+  // Matrix-core path: the query rows of a boundary-state key tile are split over dkv_split
+  // workgroups (1 or kDkvSplit), whose float32 partial dK/dV go to their own slot
+  // [dkv_split][n_chunks][H * hd] of dkb_part / dvb_part and are summed by a finalize launch.
+  int dkv_split;
+  float* dkb_part;
+  float* dvb_part;
 };
+constexpr int kDkvSplit = 4;
+// 4-byte workspace elements the attention backward needs: delta, row_w and row_ce, plus the
+// partial sums of the split boundary tiles (bf16, hd 64/128, at most one chunk per 4 tokens).
+size_t attn_bwd_workspace_elems(int T, int H, int hd, int n_chunks, int dtype);
+int attn_bwd_dkv_split(int T, int hd, int n_chunks, int dtype);
 hipError_t launch_chunk_attn_bwd(const AttnBwdParams& p, int hd, int dtype, hipStream_t stream);
 // bf16 matrix-core backward for hd 64 and 128 (needs delta, row_w and row_ce filled).
 hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, int hd, hipStream_t stream);

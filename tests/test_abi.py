@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_and_exports_agree():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert set(names) == set(B.EXPORTS), (set(names) ^ set(B.EXPORTS))
     lib = att.lib()
     for n in names:
@@ -146,6 +146,28 @@ def test_backward_entry_points_validate_before_launch():
     assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_BAD_SHAPE
     f.mode, f.dtype = 0, 9
     assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_BAD_DTYPE
+    # workspace: size query, then a workspace below it (CAPACITY) or misaligned (BAD_SHAPE)
+    f.dtype = 1
+    f.lse = fake
+    for name in ("dout", "dq", "dk", "dv", "dkb", "dvb", "workspace"):
+        setattr(b, name, fake)
+    need = C.c_size_t(0)
+    assert lib.attamba_chunk_attn_bwd_workspace_size(C.byref(b), C.byref(need)) == 0
+    # 64 tokens, 8 chunks, 2 heads x 64 (bf16): (H + 2) T rounded up to 64, plus 8 n_chunks H hd
+    assert need.value == 256 + 8 * 8 * 2 * 64
+    b.workspace_elems = need.value - 1
+    assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_CAPACITY
+    b.workspace_elems = need.value
+    b.workspace = C.c_void_p(0x1004)
+    assert lib.attamba_chunk_attn_bwd(C.byref(b), None) == B.ERR_BAD_SHAPE
+    f.n_chunks = 64                    # one token per chunk: no split, no partial sums
+    assert lib.attamba_chunk_attn_bwd_workspace_size(C.byref(b), C.byref(need)) == 0
+    assert need.value == (2 + 2) * 64
+    f.dtype = 0                        # float32 takes the row-wise kernels
+    f.n_chunks = 8
+    assert lib.attamba_chunk_attn_bwd_workspace_size(C.byref(b), C.byref(need)) == 0
+    assert need.value == (2 + 2) * 64
+    assert lib.attamba_chunk_attn_bwd_workspace_size(None, C.byref(need)) == B.ERR_NULL_ARG
 
     s = B.ScanBwdArgs()
     a = s.fwd
