@@ -36,7 +36,7 @@ namespace {
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kChannels = kWaves * 32;    // channels per workgroup (two lanes per channel)
-constexpr int kChunksPerGroup = 16;
+constexpr int kChunksPerGroup = 8;
 
 template <int N> struct BlockLen;         // tokens per backward block (state values in VGPRs)
 template <> struct BlockLen<16> { static constexpr int value = 8; };
