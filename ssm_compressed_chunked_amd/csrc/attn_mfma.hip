@@ -37,28 +37,31 @@ using namespace mfma;
 
 constexpr int NT = 256;   // threads per workgroup
 
-// p = 2^(s c - mu) for the 32 scores of this lane, rounded to bf16 and packed as the P^T
-// operand of the second product (k-step ks: keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, in the
-// accumulator's row order); returns the lane's sum of the rounded p.
+// p = 2^(s c - mu) for the 32 scores of this lane (Scaled), or p = 2^s when the scores already
+// hold s c - mu, rounded to bf16 and packed as the P^T operand of the second product (k-step ks:
+// keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, in the accumulator's row order); returns the lane's
+// sum of the rounded p, kept in two partial sums so the additions form two short chains.
+template <bool Scaled>
 __device__ __forceinline__ float tile_exp(const f32x16 (&sacc)[2], float c, float mu,
                                           bf16x8 (&pk)[4]) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  float lt = 0.f;
+  float lt[2] = {0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c, -mu));
-      const float p1 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e + 1], c, -mu));
+      const float s0 = sacc[ks >> 1][8 * (ks & 1) + e], s1 = sacc[ks >> 1][8 * (ks & 1) + e + 1];
+      const float p0 = hw_exp2(Scaled ? fmaf(s0, c, -mu) : s0);
+      const float p1 = hw_exp2(Scaled ? fmaf(s1, c, -mu) : s1);
       const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
-      lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt, false);
+      lt[ks & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt[ks & 1], false);
       w[e >> 1] = __builtin_bit_cast(unsigned, pp);
     }
     pk[ks] = __builtin_bit_cast(bf16x8, w);
   }
-  return lt;
+  return lt[0] + lt[1];
 }
 
 #ifndef ATTN_NBUF
@@ -77,6 +80,11 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   constexpr int QS = HD / 16;     // k-steps of S^T (16 hd each)
   constexpr int OB = HD / 32;     // 32-row hd blocks of O^T
   constexpr int BM = 128;         // query rows per workgroup (4 waves x 32)
+  // hd 64: Q is taken pre-multiplied by c = scale log2(e) (rounded to bf16), and the softmax
+  // reference enters the score product as its initial accumulator, so the scores come out as
+  // s c - mc and need no per-score multiply-add. hd 128 has no registers left for the
+  // accumulator that holds -mc and keeps the multiply-add.
+  constexpr bool kFold = HD == 64;
   __shared__ Smem<HD> sm;
 
   // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. All query tiles
@@ -118,11 +126,18 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const int topb = c0 + gl.E - 1;   // last boundary key of the workgroup
 
   // Q^T operand: lane (q, hf) holds hd 16 st + 8 hf .. +7 of its row
+  const float c = p.scale * kLog2e;
   bf16x8 qf[QS];
   {
     const __bf16* qr = static_cast<const __bf16*>(p.q) + ic * hs + h * HD + 8 * hf;
 #pragma unroll
-    for (int st = 0; st < QS; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
+    for (int st = 0; st < QS; ++st) {
+      qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
+      if constexpr (kFold) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[st][e] = static_cast<__bf16>(static_cast<float>(qf[st][e]) * c);
+      }
+    }
   }
   f32x16 o[OB];
 #pragma unroll
@@ -132,7 +147,8 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   // Softmax state of the row: exponent reference mc (log2 units; -inf until the row has seen
   // a key) and the running sum l of p = 2^(s c - mc) over this lane's keys.
   float mc = -INFINITY, l = 0.f;
-  const float c = p.scale * kLog2e;
+  f32x16 minit = {};   // -mc in every entry (kFold), set whenever mc changes
+  const float cs = kFold ? 1.f : c;   // factor from the product to log2 units
 
   const __bf16* kbp = static_cast<const __bf16*>(p.kb) + h * HD;
   const __bf16* vbp = static_cast<const __bf16*>(p.vb) + h * HD;
@@ -192,7 +208,6 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
       const int lo = g.w - kbase;
       const int hi = bnd ? c0 + g.E - 1 - kbase : ic - kbase;
       f32x16 sacc[2];
-      tile_scores<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi);
       // Softmax with a lazy reference. The exact maximum is taken only while some row of the
       // wave has no reference yet, or when the tile's sum of p exceeds 2^64 (a row's scores grew
       // far past its reference; the scores are then computed again from the tile still in LDS,
@@ -203,20 +218,24 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
       float lt = 0.f;
       bool exact = __any(mc == -INFINITY);
       if (!exact) {
-        lt = tile_exp(sacc, c, mc, pk);
-        if (__any(!(lt <= 0x1p64f))) {
-          exact = true;
+        if constexpr (kFold) {
+          tile_scores_from<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi, minit, -mc);
+          lt = tile_exp<false>(sacc, 1.f, 0.f, pk);
+        } else {
           tile_scores<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi);
+          lt = tile_exp<true>(sacc, c, mc, pk);
         }
+        exact = __any(!(lt <= 0x1p64f));
       }
       if (exact) {
+        tile_scores<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi);
         float m4[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           m4[u] = fmaxf(fmaxf(fmaxf(sacc[0][4 * u], sacc[0][4 * u + 1]), sacc[0][4 * u + 2]),
                         fmaxf(fmaxf(sacc[0][4 * u + 3], sacc[1][4 * u]),
                               fmaxf(sacc[1][4 * u + 1], fmaxf(sacc[1][4 * u + 2], sacc[1][4 * u + 3]))));
-        const float tm = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
+        const float tm = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * cs;
         const float mn = fmaxf(mc, tm);
         // 0 when mc = -inf (nothing accumulated yet), also for rows that still see no key
         const float alpha = hw_exp2(mc - (mn == -INFINITY ? 0.f : mn));
@@ -226,7 +245,11 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
           for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
         l *= alpha;
         mc = mn;
-        lt = tile_exp(sacc, c, mc == -INFINITY ? 0.f : mc, pk);
+        lt = tile_exp<true>(sacc, cs, mc == -INFINITY ? 0.f : mc, pk);
+        if constexpr (kFold) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) minit[v] = -mc;
+        }
       }
       l += lt;
       // O^T += V^T P^T; k-step ks covers keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, and V^T is
