@@ -37,11 +37,10 @@ using namespace mfma;
 
 constexpr int NT = 256;   // threads per workgroup
 
-// p = 2^(s c - mu) for the 32 scores of this lane (Scaled), or p = 2^s when the scores already
-// hold s c - mu, rounded to bf16 and packed as the P^T operand of the second product (k-step ks:
-// keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, in the accumulator's row order); returns the lane's
-// sum of the rounded p, kept in two partial sums so the additions form two short chains.
-template <bool Scaled>
+// p = 2^(s c - mu) for the 32 scores of this lane, rounded to bf16 and packed as the P^T
+// operand of the second product (k-step ks: keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, in the
+// accumulator's row order); returns the lane's sum of the rounded p, kept as two partial sums
+// so that the additions form two short dependency chains.
 __device__ __forceinline__ float tile_exp(const f32x16 (&sacc)[2], float c, float mu,
                                           bf16x8 (&pk)[4]) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -52,9 +51,8 @@ __device__ __forceinline__ float tile_exp(const f32x16 (&sacc)[2], float c, floa
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float s0 = sacc[ks >> 1][8 * (ks & 1) + e], s1 = sacc[ks >> 1][8 * (ks & 1) + e + 1];
-      const float p0 = hw_exp2(Scaled ? fmaf(s0, c, -mu) : s0);
-      const float p1 = hw_exp2(Scaled ? fmaf(s1, c, -mu) : s1);
+      const float p0 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c, -mu));
+      const float p1 = hw_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e + 1], c, -mu));
       const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
       lt[ks & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lt[ks & 1], false);
       w[e >> 1] = __builtin_bit_cast(unsigned, pp);
@@ -80,11 +78,6 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   constexpr int QS = HD / 16;     // k-steps of S^T (16 hd each)
   constexpr int OB = HD / 32;     // 32-row hd blocks of O^T
   constexpr int BM = 128;         // query rows per workgroup (4 waves x 32)
-  // hd 64: Q is taken pre-multiplied by c = scale log2(e) (rounded to bf16), and the softmax
-  // reference enters the score product as its initial accumulator, so the scores come out as
-  // s c - mc and need no per-score multiply-add. hd 128 has no registers left for the
-  // accumulator that holds -mc and keeps the multiply-add.
-  constexpr bool kFold = HD == 64;
   __shared__ Smem<HD> sm;
 
   // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. All query tiles
@@ -126,18 +119,11 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   const int topb = c0 + gl.E - 1;   // last boundary key of the workgroup
 
   // Q^T operand: lane (q, hf) holds hd 16 st + 8 hf .. +7 of its row
-  const float c = p.scale * kLog2e;
   bf16x8 qf[QS];
   {
     const __bf16* qr = static_cast<const __bf16*>(p.q) + ic * hs + h * HD + 8 * hf;
 #pragma unroll
-    for (int st = 0; st < QS; ++st) {
-      qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
-      if constexpr (kFold) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[st][e] = static_cast<__bf16>(static_cast<float>(qf[st][e]) * c);
-      }
-    }
+    for (int st = 0; st < QS; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
   }
   f32x16 o[OB];
 #pragma unroll
@@ -147,8 +133,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   // Softmax state of the row: exponent reference mc (log2 units; -inf until the row has seen
   // a key) and the running sum l of p = 2^(s c - mc) over this lane's keys.
   float mc = -INFINITY, l = 0.f;
-  f32x16 minit = {};   // -mc in every entry (kFold), set whenever mc changes
-  const float cs = kFold ? 1.f : c;   // factor from the product to log2 units
+  const float c = p.scale * kLog2e;
 
   const __bf16* kbp = static_cast<const __bf16*>(p.kb) + h * HD;
   const __bf16* vbp = static_cast<const __bf16*>(p.vb) + h * HD;
@@ -210,21 +195,18 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
       f32x16 sacc[2];
       // Softmax with a lazy reference. The exact maximum is taken only while some row of the
       // wave has no reference yet, or when the tile's sum of p exceeds 2^64 (a row's scores grew
-      // far past its reference; the scores are then computed again from the tile still in LDS,
-      // so they need not stay in registers); otherwise p = 2^(s c - mc) is used as is: l and
+      // far past its reference); otherwise p = 2^(s c - mc) is used as is: l and
       // O^T share mc, so the result is exact, and p <= 2^64 keeps every value finite. Values of
       // p far below 1 stay normal floats (bf16 and float32 share the exponent range).
+      // The exact path computes the scores again from the tile still in LDS: with one place
+      // where scores are made per path, none stay live across the branch, which keeps the kernel
+      // at 126 VGPRs (4 waves per SIMD instead of 3 at 160).
       bf16x8 pk[4];
       float lt = 0.f;
       bool exact = __any(mc == -INFINITY);
       if (!exact) {
-        if constexpr (kFold) {
-          tile_scores_from<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi, minit, -mc);
-          lt = tile_exp<false>(sacc, 1.f, 0.f, pk);
-        } else {
-          tile_scores<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi);
-          lt = tile_exp<true>(sacc, c, mc, pk);
-        }
+        tile_scores<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi);
+        lt = tile_exp(sacc, c, mc, pk);
         exact = __any(!(lt <= 0x1p64f));
       }
       if (exact) {
@@ -235,7 +217,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
           m4[u] = fmaxf(fmaxf(fmaxf(sacc[0][4 * u], sacc[0][4 * u + 1]), sacc[0][4 * u + 2]),
                         fmaxf(fmaxf(sacc[0][4 * u + 3], sacc[1][4 * u]),
                               fmaxf(sacc[1][4 * u + 1], fmaxf(sacc[1][4 * u + 2], sacc[1][4 * u + 3]))));
-        const float tm = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * cs;
+        const float tm = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
         const float mn = fmaxf(mc, tm);
         // 0 when mc = -inf (nothing accumulated yet), also for rows that still see no key
         const float alpha = hw_exp2(mc - (mn == -INFINITY ? 0.f : mn));
@@ -245,11 +227,7 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
           for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
         l *= alpha;
         mc = mn;
-        lt = tile_exp<true>(sacc, cs, mc == -INFINITY ? 0.f : mc, pk);
-        if constexpr (kFold) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) minit[v] = -mc;
-        }
+        lt = tile_exp(sacc, c, mc == -INFINITY ? 0.f : mc, pk);
       }
       l += lt;
       // O^T += V^T P^T; k-step ks covers keys 16 ks + {4 hf .. +3, 8 + 4 hf .. +3}, and V^T is

@@ -98,17 +98,17 @@ struct TileCopy {
   }
 };
 
-// S^T = K Q^T for one tile (keys on accumulator rows, this lane's query on its column), plus
-// an offset: the mask enters as the initial accumulator, base for a visible key and -inf for a
-// hidden one (accumulator row v of block kb is key base + 4 hf + C(kb, v), C = 32 kb + 8 (v / 4)
-// + v % 4); fully visible tiles start from init, which holds base in all 16 entries. Visible:
-// lo <= C <= hi (boundary tiles only test hi). koff: this lane's operand offsets for key block 0;
-// block 1 lies 32 rows further (the swizzle repeats every 16 rows).
+// S^T = K Q^T for one tile (keys on accumulator rows, this lane's query on its column). The mask
+// enters as the initial accumulator: 0 for a visible key, -inf for a hidden one (accumulator
+// row v of block kb is key base + 4 hf + C(kb, v), C = 32 kb + 8 (v / 4) + v % 4); fully
+// visible tiles start from the zero accumulator. Visible: lo <= C <= hi (boundary tiles only
+// test hi). koff: this lane's operand offsets for key block 0; block 1 lies 32 rows further
+// (the swizzle repeats every 16 rows).
 template <int HD, int QS>
-__device__ __forceinline__ void tile_scores_from(f32x16 (&sacc)[2], const __bf16* sk,
-                                                 const int (&koff)[QS], const bf16x8 (&qf)[QS],
-                                                 bool full, bool bnd, int lo, int hi,
-                                                 const f32x16& init, float base) {
+__device__ __forceinline__ void tile_scores(f32x16 (&sacc)[2], const __bf16* sk,
+                                            const int (&koff)[QS], const bf16x8 (&qf)[QS],
+                                            bool full, bool bnd, int lo, int hi) {
+  const f32x16 zero16 = {};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     bf16x8 ka[QS];
@@ -116,19 +116,19 @@ __device__ __forceinline__ void tile_scores_from(f32x16 (&sacc)[2], const __bf16
     for (int st = 0; st < QS; ++st)
       ka[st] = *reinterpret_cast<const bf16x8*>(sk + koff[st] + 32 * HD * kb);
     if (full) {
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], init, 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], zero16, 0, 0, 0);
     } else {
       if (bnd) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
-          sacc[kb][v] = C <= hi ? base : -INFINITY;
+          sacc[kb][v] = C <= hi ? 0.f : -INFINITY;
         }
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int C = 32 * kb + 8 * (v >> 2) + (v & 3);
-          sacc[kb][v] = (C >= lo && C <= hi) ? base : -INFINITY;
+          sacc[kb][v] = (C >= lo && C <= hi) ? 0.f : -INFINITY;
         }
       }
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], sacc[kb], 0, 0, 0);
@@ -137,15 +137,6 @@ __device__ __forceinline__ void tile_scores_from(f32x16 (&sacc)[2], const __bf16
     for (int st = 1; st < QS; ++st)
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf[st], sacc[kb], 0, 0, 0);
   }
-}
-
-// The plain scores: visible keys start from 0.
-template <int HD, int QS>
-__device__ __forceinline__ void tile_scores(f32x16 (&sacc)[2], const __bf16* sk,
-                                            const int (&koff)[QS], const bf16x8 (&qf)[QS],
-                                            bool full, bool bnd, int lo, int hi) {
-  const f32x16 zero16 = {};
-  tile_scores_from<HD, QS>(sacc, sk, koff, qf, full, bnd, lo, hi, zero16, 0.f);
 }
 
 }  // namespace mfma
