@@ -7,7 +7,8 @@
 //      SSM_K and SSM_V step, write the token's key/value into its window slot and, at a chunk
 //      end, append it as the next boundary state;
 //   2. decode_attn_split: the key list of each (sequence, head) — boundary states 0..E-1 then
-//      window positions w..pos — is cut into splits of kSplit keys; each workgroup streams one
+//      window positions w..pos — is cut into splits (256 keys, or 1024 for bf16 when the grid
+//      still holds enough workgroups); each workgroup streams one
 //      split (16-byte loads, hd/8 lanes per key row, so one wave instruction reads several
 //      whole rows) and leaves an unnormalised partial (o, running max, sum) in the workspace;
 //   3. decode_combine: merges the partials of every (sequence, head).
@@ -18,7 +19,9 @@
 namespace attamba {
 namespace {
 
-constexpr int kSplit = 256;          // keys per split workgroup
+constexpr int kSplit = 256;          // keys per split workgroup (the finest split)
+constexpr int kSplitWide = 1024;     // bf16 caches whose grid keeps kWideMinGroups workgroups
+constexpr int kWideMinGroups = 4096; // about two rounds of resident workgroups on 256 CUs
 constexpr int kSplitThreads = 256;
 constexpr int kUpdLanes = 4;         // lanes per (sequence, channel) in the state update
 
@@ -109,12 +112,13 @@ __device__ __forceinline__ size_t key_off(const attamba_decode_cache& c, const D
   return (bh * c.L + sl) * c.hd;
 }
 
-// One split of kSplit keys of one (sequence, head). A key row is read by LPK lanes with 16-byte
+// One split of SPLIT keys of one (sequence, head). A key row is read by LPK lanes with 16-byte
 // loads (KPW rows per wave instruction); the loads of NB rows per lane are issued together
 // before any is used, for both the K pass (scores) and the V pass (P V). Every cache row is read
 // once per step, so the loads are non-temporal (no cache allocation): 6.3 TB/s against 5.9 TB/s
-// with ordinary loads at the 4.4 GB per step of a 32 x 32768-token batch.
-template <typename T, int HD>
+// with ordinary loads at the 4.4 GB per step of a 32 x 32768-token batch. Splits of 1024 keys
+// keep four times the bytes per workgroup in flight between its two reductions: 6.7 TB/s there.
+template <typename T, int HD, int SPLIT>
 __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
     attamba_decode_cache c, attamba_decode_inputs in, DecodeLaunch dl, int max_splits) {
   constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte load
@@ -122,9 +126,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   constexpr int KPW = kWave / LPK;             // key rows per wave instruction
   constexpr int NW = kSplitThreads / kWave;
   constexpr int KPB = KPW * NW;                // key rows per workgroup iteration
-  constexpr int NIT = kSplit / KPB;            // iterations per split
+  constexpr int NIT = SPLIT / KPB;             // iterations per split
   constexpr int NB = NIT < 8 ? NIT : 8;        // iterations whose loads fly together
-  __shared__ float s_p[kSplit];
+  __shared__ float s_p[SPLIT];
   __shared__ float s_red[NW];
   __shared__ float s_acc[NW][KPW][HD];
 
@@ -133,8 +137,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   const int sub = lane % LPK, grp = lane / LPK;
   const size_t bh = static_cast<size_t>(b) * c.H + h;
   const int n_keys = dl.E + dl.n_window;
-  const int k0 = sp * kSplit;
-  const int nk = min(kSplit, n_keys - k0);
+  const int k0 = sp * SPLIT;
+  const int nk = min(SPLIT, n_keys - k0);
   float* part = static_cast<float*>(c.workspace) + (bh * max_splits + sp) * (HD + 2);
   if (nk <= 0) {   // no key in this split (only when the whole list is empty)
     for (int e = tid; e < HD; e += kSplitThreads) part[e] = 0.f;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_red[w]);
   __syncthreads();
   float sum = 0.f;
-  for (int k = tid; k < kSplit; k += kSplitThreads) {
+  for (int k = tid; k < SPLIT; k += kSplitThreads) {
     const float pr = k < nk ? hw_exp2(s_p[k] - mx) : 0.f;
     s_p[k] = pr;
     sum += pr;
@@ -273,14 +277,30 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(attamba_decode_cache
 
 template <typename T, int N, int HD>
 hipError_t launch_typed(const attamba_decode_cache& c, const attamba_decode_inputs& in,
-                        const DecodeLaunch& dl, hipStream_t stream) {
+                        const DecodeLaunch& dl_in, hipStream_t stream) {
+  // the workspace holds max_splits partials per (sequence, head), counted at the finest split
   const int max_splits = decode_max_splits(c.cap, c.L);
+  const int n_keys = dl_in.E + dl_in.n_window;
+  const bool wide = sizeof(T) == 2 &&
+                    static_cast<long long>(c.B) * c.H * ceil_div(n_keys, kSplitWide) >= kWideMinGroups;
+  DecodeLaunch dl = dl_in;
+  dl.n_splits = max(1, ceil_div(n_keys, wide ? kSplitWide : kSplit));
   hipLaunchKernelGGL((decode_update_kernel<T, N>), dim3(c.d * kUpdLanes / 256, c.B), dim3(256), 0,
                      stream, c, in, dl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((decode_attn_split_kernel<T, HD>), dim3(dl.n_splits, c.H, c.B),
-                     dim3(kSplitThreads), 0, stream, c, in, dl, max_splits);
+  bool launched = false;
+  if constexpr (sizeof(T) == 2) {
+    if (wide) {
+      hipLaunchKernelGGL((decode_attn_split_kernel<T, HD, kSplitWide>), dim3(dl.n_splits, c.H, c.B),
+                         dim3(kSplitThreads), 0, stream, c, in, dl, max_splits);
+      launched = true;
+    }
+  }
+  if (!launched) {
+    hipLaunchKernelGGL((decode_attn_split_kernel<T, HD, kSplit>), dim3(dl.n_splits, c.H, c.B),
+                       dim3(kSplitThreads), 0, stream, c, in, dl, max_splits);
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_combine_kernel<T, HD>), dim3(c.H, c.B), dim3(HD), 0, stream, c, in,
@@ -366,13 +386,10 @@ size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L) {
 
 hipError_t launch_decode_step(const attamba_decode_cache& c, const attamba_decode_inputs& in,
                               const DecodeLaunch& dl_in, hipStream_t stream) {
-  DecodeLaunch dl = dl_in;
-  dl.n_splits = ceil_div(dl.E + dl.n_window, kSplit);
-  if (dl.n_splits == 0) dl.n_splits = 1;
   if (c.dtype == ATTAMBA_BF16) {
-    return c.N == 16 ? launch_hd<__bf16, 16>(c, in, dl, stream) : launch_hd<__bf16, 32>(c, in, dl, stream);
+    return c.N == 16 ? launch_hd<__bf16, 16>(c, in, dl_in, stream) : launch_hd<__bf16, 32>(c, in, dl_in, stream);
   }
-  return c.N == 16 ? launch_hd<float, 16>(c, in, dl, stream) : launch_hd<float, 32>(c, in, dl, stream);
+  return c.N == 16 ? launch_hd<float, 16>(c, in, dl_in, stream) : launch_hd<float, 32>(c, in, dl_in, stream);
 }
 
 }  // namespace attamba

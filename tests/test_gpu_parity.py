@@ -363,6 +363,49 @@ def test_decode_rejects_full_cache_and_bad_mirror():
     assert e.value.status == 2
 
 
+def test_decode_full_size_wide_split():
+    """decode_bf16 at full size (32 sequences x 32 heads, 8 192 boundary states plus a window of
+    256 per sequence): the key list is cut into splits of 1 024 keys, the launch the decode bench
+    times. Two steps from a random cache; sequences 0 and 31 are checked against the oracle's
+    decode step on the same cache contents."""
+    from workloads import DECODE_CONFIGS, make_decode
+    cfg = DECODE_CONFIGS["decode_bf16"]
+    say(f"decode full size B={cfg.B} H={cfg.H} hd={cfg.hd} ctx={cfg.ctx}")
+    P, L, layer = cfg.P, cfg.L, cfg.layer_idx
+    ends = [j for j in range(cfg.ctx) if oracle.is_chunk_end_at(j, P, layer)]
+    n_bound = len(ends)
+    assert n_bound == att.count_chunks([0, cfg.ctx], P, layer)
+    steps = 2
+    inp = make_decode(cfg, n_bound=n_bound, steps=steps, device="cuda")
+    cache = att.DecodeCache(cfg.B, cfg.H, cfg.hd, cfg.N, P, L, layer, n_bound + 4, torch.bfloat16,
+                            inp.param, pos=cfg.ctx, n_bound=n_bound)
+    cache.kb[:, :, :n_bound] = inp.kb
+    cache.vb[:, :, :n_bound] = inp.vb
+    cache.kw.copy_(inp.kw)
+    cache.vw.copy_(inp.vw)
+    act = {k: v.cuda() for k, v in inp.act.items()}
+    outs = []
+    for s in range(steps):
+        out = att.decode_step(cache, act["q"][s].view(cfg.B, cfg.H, cfg.hd).contiguous(), act["x"][s],
+                              act["dt_k"][s], act["dt_v"][s], act["bm_k"][s], act["cm_k"][s],
+                              act["bm_v"][s], act["cm_v"][s])
+        outs.append(out.float().cpu().numpy())
+    torch.cuda.synchronize()
+    par = {k: v.double().numpy() for k, v in inp.param.items()}
+    for b in (0, cfg.B - 1):
+        kb = inp.kb[b].double().cpu().numpy()          # [H, n_bound, hd]
+        vb = inp.vb[b].double().cpu().numpy()
+        kw = inp.kw[b].double().cpu().numpy()          # [H, L, hd]
+        vw = inp.vw[b].double().cpu().numpy()
+        st = oracle.DecodeSeq(pos=cfg.ctx, h_k=np.zeros((cfg.d, cfg.N)), h_v=np.zeros((cfg.d, cfg.N)))
+        st.bounds = [(j, kb[:, idx], vb[:, idx]) for idx, j in enumerate(ends)]
+        st.recent = [(j, kw[:, j % L], vw[:, j % L]) for j in range(cfg.ctx - L, cfg.ctx)]
+        for s in range(steps):
+            tok = {k: v[s, b].double().numpy() for k, v in inp.act.items()}
+            ref = oracle.decode_step(st, par, tok, cfg.H, cfg.hd, P, layer, L)
+            check_close(outs[s][b], ref, "bf16", f"full-size decode sequence {b} step {s}")
+
+
 def test_decode_snapshot_resume_bit_exact():
     """The cache buffers plus the host mirrors (pos, n_bound) are the whole decode state: a
     snapshot restored after more steps replays those steps with identical outputs."""
