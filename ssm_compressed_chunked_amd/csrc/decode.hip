@@ -127,7 +127,8 @@ __global__ __launch_bounds__(kSplitThreads) void decode_attn_split_kernel(
   constexpr int NW = kSplitThreads / kWave;
   constexpr int KPB = KPW * NW;                // key rows per workgroup iteration
   constexpr int NIT = SPLIT / KPB;             // iterations per split
-  constexpr int NB = NIT < 8 ? NIT : 8;        // iterations whose loads fly together
+  // iterations whose loads fly together (16 rows per lane in the 1024-key split: +0.7 %)
+  constexpr int NB = NIT < 8 ? NIT : (SPLIT >= 1024 ? 16 : 8);
   __shared__ float s_p[SPLIT];
   __shared__ float s_red[NW];
   __shared__ float s_acc[NW][KPW][HD];
