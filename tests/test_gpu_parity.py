@@ -363,13 +363,16 @@ def test_decode_rejects_full_cache_and_bad_mirror():
     assert e.value.status == 2
 
 
-def test_decode_full_size_wide_split():
+@pytest.mark.parametrize("H,hd,ctx", [(32, 128, 32768), (64, 64, 8192), (128, 32, 8192)])
+def test_decode_full_size_wide_split(H, hd, ctx):
     """decode_bf16 at full size (32 sequences x 32 heads, 8 192 boundary states plus a window of
-    256 per sequence): the key list is cut into splits of 1 024 keys, the launch the decode bench
-    times. Two steps from a random cache; sequences 0 and 31 are checked against the oracle's
-    decode step on the same cache contents."""
+    256 per sequence), and the same width split into 64 heads of 64 or 128 heads of 32 at a
+    quarter of the context: the key lists are cut into splits of 1 024 keys, the launch the
+    decode bench times. Two steps from a random cache; sequences 0 and 31 are checked against
+    the oracle's decode step on the same cache contents."""
     from workloads import DECODE_CONFIGS, make_decode
-    cfg = DECODE_CONFIGS["decode_bf16"]
+    cfg = DECODE_CONFIGS["decode_bf16"].with_(H=H, hd=hd, ctx=ctx)
+    assert cfg.H * cfg.hd == cfg.d
     say(f"decode full size B={cfg.B} H={cfg.H} hd={cfg.hd} ctx={cfg.ctx}")
     P, L, layer = cfg.P, cfg.L, cfg.layer_idx
     ends = [j for j in range(cfg.ctx) if oracle.is_chunk_end_at(j, P, layer)]
