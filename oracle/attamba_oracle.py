@@ -202,8 +202,9 @@ def selective_scan_backward(x, dt, dt_bias, A, Bm, Cm, D, chunk_cu, gy):
 
 
 def boundary_states(y, chunk_cu):
-    """One state per chunk: the SSM output at the chunk's last token (the review's
-    K^(p)[-1]: "the SSM output after processing the entire chunk")."""
+    """One state per chunk: the SSM output y at the chunk's last token (pith.science review,
+    Referee Report, comment on Eq. 7: the boundary state K^(p)[-1] is the output once the
+    whole chunk has been processed)."""
     return y[np.asarray(chunk_cu[1:], dtype=np.int64) - 1]
 
 

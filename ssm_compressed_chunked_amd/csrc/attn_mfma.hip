@@ -62,10 +62,7 @@ __device__ __forceinline__ float tile_exp(const f32x16 (&sacc)[2], float c, floa
   return lt[0] + lt[1];
 }
 
-#ifndef ATTN_NBUF
-#define ATTN_NBUF 2
-#endif
-constexpr int NBUF = ATTN_NBUF;   // tiles in LDS: the current one and the copies in flight
+constexpr int NBUF = 2;   // tiles in LDS: the current one and the copy in flight
 
 template <int HD>
 struct Smem {

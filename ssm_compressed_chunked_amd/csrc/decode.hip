@@ -21,7 +21,10 @@ namespace {
 
 constexpr int kSplit = 256;          // keys per split workgroup (the finest split)
 constexpr int kSplitWide = 1024;     // bf16 caches whose grid keeps kWideMinGroups workgroups
-constexpr int kWideMinGroups = 4096; // about two rounds of resident workgroups on 256 CUs
+// The 1024-key kernel takes 234 VGPRs (2 waves per SIMD), so a CU holds two of its 4-wave
+// workgroups and the chip 512; 4096 workgroups keep the grid at least 8 such rounds deep, so
+// the longer splits do not leave a ragged last round. Below that the 256-key split is used.
+constexpr int kWideMinGroups = 8 * 2 * 256;
 constexpr int kSplitThreads = 256;
 constexpr int kUpdLanes = 4;         // lanes per (sequence, channel) in the state update
 

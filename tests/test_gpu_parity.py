@@ -202,9 +202,24 @@ def test_h_last_handoff():
             assert np.abs(got[si] - ref).max() <= 1e-3 * (np.abs(ref).max() + 1e-6)
 
 
-# ------------------------------------------------------- full-size workloads, sampled checks
+# --------------------------------------------------- full-size workloads, every sequence
+def _attn_heads(cfg, s):
+    """Heads checked on every row of sequence s: all of them at train_bf16 (n = 2048), else two
+    that differ from one sequence to the next."""
+    if cfg.n <= 2048:
+        return list(range(cfg.H))
+    a = (5 * s) % cfg.H
+    return sorted({a, cfg.H - 1 - a})
+
+
 @pytest.mark.parametrize("cfg", [TRAIN_BF16, PREFILL_BF16, VARCHUNK_BF16], ids=lambda c: c.name)
-def test_full_size_sampled(cfg):
+def test_full_size_every_sequence(cfg):
+    """The full workloads in the launch configuration the benchmark times (segmentation, the
+    scan with boundary outputs, the attention with its LSE). For every sequence: y_k, y_v at
+    every token and kb, vb at every chunk against the oracle's scan of that whole sequence;
+    O and LSE of every row for some heads (all heads at train_bf16), and of 44 rows (the first
+    two, the last two and 40 drawn) for every head, against the oracle's attention over the
+    oracle's own keys and values."""
     say(f"full-size {cfg.name}")
     inp = make_prefill(cfg)
     act, par = to_dev(inp)
@@ -216,33 +231,42 @@ def test_full_size_sampled(cfg):
     ref_cu, ref_tc, ref_ie = oracle.segment(inp.seq_cu, P, cfg.layer_idx, inp.chunk_lens)
     np.testing.assert_array_equal(res["layout"].chunk_cu.cpu().numpy(), ref_cu)
     np.testing.assert_array_equal(res["layout"].token_chunk.cpu().numpy(), ref_tc)
+    np.testing.assert_array_equal(res["layout"].is_end.cpu().numpy(), ref_ie)
     f = f64_inputs(inp)
-    T, n = cfg.T, len(ref_cu) - 1
+    T, H, hd = cfg.T, cfg.H, cfg.hd
+    got = {k: res["scan"][k].float().cpu().numpy() for k in ("y_k", "y_v", "kb", "vb")}
+    out_all = res["out"].float().cpu().numpy()
+    lse_all = res["lse"].cpu().numpy()
+    q3 = f["q"].reshape(T, H, hd)
     rng = np.random.default_rng(0)
-    # scan: sampled chunks (the state restarts at every chunk, so each is checked on its own)
-    for q in sorted(set(rng.integers(0, n, 6).tolist()) | {0, n - 1}):
-        a, b = int(ref_cu[q]), int(ref_cu[q + 1])
+    for si in range(len(inp.seq_cu) - 1):
+        a, b = int(inp.seq_cu[si]), int(inp.seq_cu[si + 1])
+        qa, qb = int(ref_tc[a]), int(ref_tc[b - 1]) + 1          # the sequence's chunks
+        ys = {}
         for tag in ("k", "v"):
             y, _ = oracle.selective_scan(f["x"], f[f"dt_{tag}"], f[f"bias_{tag}"], f[f"A_{tag}"],
                                          f[f"bm_{tag}"], f[f"cm_{tag}"], f[f"D_{tag}"], ref_cu,
                                          t_begin=a, t_end=b)
-            check_close(res["scan"][f"y_{tag}"][a:b].float().cpu().numpy(), y, cfg.dtype,
-                        f"y_{tag} chunk {q}")
-    # attention: sampled rows of every sequence, against the oracle over its own K/V
-    seq0 = int(inp.seq_cu[0]), int(inp.seq_cu[1])
-    a, b = seq0
-    yk, _ = oracle.selective_scan(f["x"], f["dt_k"], f["bias_k"], f["A_k"], f["bm_k"], f["cm_k"],
-                                  f["D_k"], ref_cu, t_begin=a, t_end=b)
-    yv, _ = oracle.selective_scan(f["x"], f["dt_v"], f["bias_v"], f["A_v"], f["bm_v"], f["cm_v"],
-                                  f["D_v"], ref_cu, t_begin=a, t_end=b)
-    rows = np.unique(np.concatenate([rng.integers(a, b, 40), [a, a + 1, b - 1, b - 2]]))
-    H, hd = cfg.H, cfg.hd
-    k3 = np.zeros((T, H, hd)); v3 = np.zeros((T, H, hd))
-    k3[a:b] = yk.reshape(-1, H, hd); v3[a:b] = yv.reshape(-1, H, hd)
-    out, lse = oracle.chunk_attention(f["q"].reshape(T, H, hd), k3, v3, inp.seq_cu, ref_tc, ref_ie,
-                                      cfg.L, cfg.mode, rows=rows)
-    check_close(res["out"][rows].float().cpu().numpy(), out, cfg.dtype, "out rows")
-    check_close(res["lse"][:, rows].cpu().numpy(), lse, cfg.dtype, "lse rows")
+            ys[tag] = y
+            check_close(got[f"y_{tag}"][a:b], y, cfg.dtype, f"y_{tag} of sequence {si}")
+            bref = oracle.boundary_states(y, ref_cu[qa:qb + 1] - a)
+            check_close(got[f"{tag}b"][qa:qb], bref, cfg.dtype, f"{tag}b of sequence {si}")
+        # attention of this sequence over the oracle's keys and values (rows of the other
+        # sequences never see them, so zeros stand in there)
+        k3 = np.zeros((T, H, hd)); v3 = np.zeros((T, H, hd))
+        k3[a:b] = ys["k"].reshape(-1, H, hd)
+        v3[a:b] = ys["v"].reshape(-1, H, hd)
+        heads = _attn_heads(cfg, si)
+        o_h, l_h = oracle.chunk_attention(q3[:, heads], k3[:, heads], v3[:, heads], inp.seq_cu,
+                                          ref_tc, ref_ie, cfg.L, cfg.mode, rows=np.arange(a, b))
+        check_close(out_all[a:b][:, heads], o_h, cfg.dtype, f"O of sequence {si}, heads {heads}")
+        check_close(lse_all[heads, a:b], l_h, cfg.dtype, f"LSE of sequence {si}, heads {heads}")
+        rows = np.unique(np.concatenate([rng.integers(a, b, 40), [a, a + 1, b - 2, b - 1]]))
+        o_r, l_r = oracle.chunk_attention(q3, k3, v3, inp.seq_cu, ref_tc, ref_ie, cfg.L,
+                                          cfg.mode, rows=rows)
+        check_close(out_all[rows], o_r, cfg.dtype, f"O rows of sequence {si}, all heads")
+        check_close(lse_all[:, rows], l_r, cfg.dtype, f"LSE rows of sequence {si}, all heads")
+        say(f"  sequence {si}: scan and attention match")
 
 
 @pytest.mark.parametrize("cfg", [PREFILL_BF16, VARCHUNK_BF16], ids=lambda c: c.name)
