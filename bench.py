@@ -13,6 +13,7 @@ train_bf16 forward's working set fits in the 256 MB MALL, so both are reported).
     python bench.py --workload layer_bf16       # projections + KV-SSM forward from the layer input
     python bench.py --workload train_step_bf16  # forward + backward at the M_train workload
     python bench.py --workload copy             # reference bandwidth (512 MiB device copy)
+    python bench.py --workload valu_issue       # clocks per wave64 VALU / MFMA instruction
 """
 from __future__ import annotations
 
@@ -38,8 +39,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 VALU_SLOTS_PER_S = 256 * 4 * 32 * 2.4e9
 # VALU issue slots per state update of the scan: multiply for the exponent, v_exp_f32, multiply
 # for the input term, FMA state, FMA output. A wave64 v_exp_f32 occupies the SIMD 2.75 times as
-# long as a wave64 FMA (5.5 vs 2.0 clocks, measured at 4 waves per SIMD), so it counts 2.75.
+# long as a wave64 FMA (5.5 vs 2.0 clocks at 4 waves per SIMD; `--workload valu_issue` measures
+# both, and the whole update, on the part), so it counts 2.75.
 SLOTS_PER_UPDATE = 6.75
+PROBE_LIB = os.path.join(ROOT, "ssm_compressed_chunked_amd", "libattamba_probe.so")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -208,22 +211,8 @@ def bench_prefill(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # whole-job timing: exactly K steps, synchronised on both sides
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # per-kernel durations with HIP events on the launch stream (separate pass, same work)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    seg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    # the same steps with the caches flushed before each one (a 512 MiB write evicts the L2s and
-    # the 256 MB MALL, which can otherwise hold a small configuration's whole working set)
+    # The same steps with the caches flushed before each one (a 512 MiB write evicts the L2s and
+    # the 256 MB MALL, which can otherwise hold a small configuration's whole working set).
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     evf = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for k, e in enumerate(evf):
@@ -236,6 +225,18 @@ def bench_prefill(args):
                               "chunk_attn": round(float(np.mean([e[2].elapsed_time(e[3]) for e in evf])) * 1e3, 2)},
                "step_us": round(float(np.mean([e[0].elapsed_time(e[3]) for e in evf])) * 1e3, 2),
                "note": "HIP events around each step after a 512 MiB device write; value and kernels_us are hot"}
+    # Whole-job timing: exactly K steps, synchronised on both sides. HIP events recorded on the
+    # launch stream between the kernels of these same steps give the per-kernel durations.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
     ms = wall * 1e3 / args.steps
     tok_s = T / (wall / args.steps)
@@ -252,11 +253,17 @@ def bench_prefill(args):
     traffic = measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"], args.workload)
     attn_traffic = measured_traffic("attn_mfma_kernel", ["attn_mfma.hip", "attn_geom.h", "attn_tiles.h",
                                                          "common.h"], args.workload)
-    roofline = {"bound": "alu", "kernel": "kvssm_scan_kernel", "achieved": round(scan_alu_tslots, 3),
-                "peak": round(alu_peak, 3), "unit": "T VALU-slot/s", "frac": round(scan_alu_tslots / alu_peak, 4),
+    # The scan is the dominant kernel; its roofline is HBM: algorithmic bytes per launch over
+    # its event-timed launch duration, against 8 TB/s. Its instruction-issue figure (the stream
+    # of VALU slots it must issue, against the chip's issue rate) is reported beside it.
+    roofline = {"bound": "hbm", "kernel": "kvssm_scan_kernel", "achieved": round(scan_gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                "work_per_launch": f"{updates} state updates x {SLOTS_PER_UPDATE} slots",
+                "algorithmic_bytes_per_launch": scan_bytes,
                 "avg_launch_us": round(scan_ms * 1e3, 2)}
+    scan_valu = {"achieved": round(scan_alu_tslots, 3), "peak": round(alu_peak, 3),
+                 "unit": "T VALU-slot/s", "frac": round(scan_alu_tslots / alu_peak, 4),
+                 "work_per_launch": f"{updates} state updates x {SLOTS_PER_UPDATE} slots"}
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -270,8 +277,7 @@ def bench_prefill(args):
         "kernels_us": {"segmentation": round(seg_ms * 1e3, 2), "kvssm_scan": round(scan_ms * 1e3, 2),
                        "chunk_attn": round(attn_ms * 1e3, 2)},
         "flushed": flushed,
-        "scan_hbm": {"algorithmic_bytes": scan_bytes, "GBps": round(scan_gbps, 1),
-                     "frac_of_8TBps": round(scan_gbps / HBM_PEAK_GBPS, 4)},
+        "scan_valu": scan_valu,
         "attn_mfma": {"algorithmic_flop": attn_flop, "visible_pairs_per_head": pairs,
                       "TFLOPs": round(attn_tflops, 2),
                       "frac_of_2.5PF": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -607,6 +613,111 @@ def bench_copy(args):
                       "GBps_read_plus_write": round(gbps, 1)}), flush=True)
 
 
+PROBE_OPS = {0: "v_fma_f32 VOP3 (VGPR operands)", 1: "v_fma_f32 VOP3 (one SGPR operand)",
+             2: "v_mul_f32 VOP2 (VGPR operands)", 3: "v_exp_f32 VOP3 (negated source)",
+             4: "v_mfma_f32_32x32x16_bf16",
+             5: "scan state update (v_mul, v_exp, v_mul with SGPR, v_fmac, v_fmac with SGPR)",
+             6: "v_fmac_f32 VOP2 (VGPR operands)", 7: "v_fmac_f32 VOP2 (one SGPR operand)",
+             8: "v_add_f32 VOP2 (VGPR operands)", 9: "v_exp_f32 VOP1 + v_mul_f32 VOP2 (VGPR) pair",
+             10: "v_fmamk_f32 VOP2 (literal operand)", 11: "v_cvt_pk_bf16_f32 + v_perm_b32 (two VOP3)",
+             12: "v_dot2 bf16 pairs, f32 accumulator",
+             13: "v_exp_f32 VOP3 + independent v_fmac_f32 VOP2 pair",
+             14: "v_mfma_f32_32x32x16_bf16 + 8 independent v_fmac_f32 VOP2 (per MFMA)"}
+PROBE_ITERS = {0: 20000, 1: 20000, 2: 20000, 3: 8000, 4: 2000, 5: 1000, 6: 20000, 7: 20000,
+               8: 20000, 9: 8000, 10: 20000, 11: 20000, 12: 20000, 13: 8000, 14: 2000}
+
+
+def probe_per_simd(rec, ops_per_wave, W):
+    """rec: one row per wave (clock before, after, real time before, after, HW_ID, XCC_ID).
+    Groups the waves by SIMD (XCC, shader engine, shader array, CU, SIMD: HW_ID bits 4..15),
+    keeps the SIMDs that held exactly W waves that all ran side by side (every start before
+    every end, on that SIMD's shader clock), and returns the median over them of the SIMD's busy
+    span divided by the instructions its waves issued."""
+    rec = rec.astype(np.int64)
+    key = (rec[:, 5] & 0xF) * 4096 + ((rec[:, 4] >> 4) & 0xFFF)
+    spans, counts = [], {}
+    for k in np.unique(key):
+        g = rec[key == k]
+        counts[len(g)] = counts.get(len(g), 0) + 1
+        if len(g) == W and g[:, 0].max() < g[:, 1].min():
+            spans.append((g[:, 1].max() - g[:, 0].min()) / (W * ops_per_wave))
+    dclk = (rec[:, 1] - rec[:, 0]).astype(np.float64)
+    dreal = (rec[:, 3] - rec[:, 2]).astype(np.float64)
+    return {"clocks_per_instr_per_simd": round(float(np.median(spans)), 3) if spans else None,
+            "simds_used": len(spans), "waves_per_simd_histogram": {str(k): v for k, v in sorted(counts.items())},
+            "clock_GHz": float(np.median(dclk / (dreal * 10.0)))}
+
+
+def bench_valu_issue(args):
+    """Issue cost of the instructions the scan and the attention are made of: shader clocks per
+    wave64 instruction per SIMD, with W = 1, 2, 4, 8 waves per SIMD, each wave running
+    independent chains (libattamba_probe.so, read from the kernel's own s_memtime clock). Also
+    the scan's whole state update in FMA slots, the figure its instruction-issue roofline uses."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: run the build first")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.attamba_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.attamba_probe_ops_per_iter.argtypes = [ctypes.c_int]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(0)
+    vin = torch.from_numpy(np.concatenate([rng.uniform(0.5, 1.0, 128), np.full(64, 0.3)])
+                           .astype(np.float32)).cuda()
+    rows = (ctypes.c_float * 32)(*rng.uniform(-1.0, 1.0, 32).astype(np.float32).tolist())
+    stream = torch.cuda.current_stream()
+    res, clock_ghz = {}, []
+    for op, name in PROBE_OPS.items():
+        per_iter = lib.attamba_probe_ops_per_iter(op)
+        res[name] = {}
+        for W in (1, 2, 4, 8):
+            blocks = n_cu * W            # 4-wave workgroups: W waves on every SIMD
+            out = torch.zeros(6 * 4 * blocks, dtype=torch.int64, device="cuda")
+            sink = torch.empty(256 * blocks, dtype=torch.float32, device="cuda")
+            for _ in range(2):           # the first run ramps the clocks
+                rc = lib.attamba_probe_issue(op, blocks, PROBE_ITERS[op], 0.3, vin.data_ptr(),
+                                             rows, out.data_ptr(), sink.data_ptr(),
+                                             ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"probe launch failed ({rc})")
+                torch.cuda.synchronize()
+            r = probe_per_simd(out.cpu().numpy().reshape(-1, 6), per_iter * PROBE_ITERS[op], W)
+            clock_ghz.append(r.pop("clock_GHz"))
+            res[name][f"W{W}"] = r
+    def clk(op, w="W4"):
+        return res[PROBE_OPS[op]][w]["clocks_per_instr_per_simd"]
+
+    def ratio(a, b):
+        return None if a is None or b is None else round(a / b, 3)
+
+    fma = clk(0)
+    derived = {
+        "fma_vop3_clocks_W4": fma,
+        "fmac_vop2_clocks_W4": clk(6),
+        "mul_vop2_clocks_W4": clk(2),
+        "exp_vop1_clocks_W4": None if clk(9) is None or clk(2) is None else round(clk(9) - clk(2), 3),
+        "fmamk_literal_clocks_W4": clk(10),
+        "cvt_pk_bf16_clocks_W4": clk(11),
+        "dot2_bf16_clocks_W4": clk(12),
+        "exp_plus_fmac_pair_clocks_W4": clk(13),
+        "mfma_plus_8_fmac_clocks_W1": clk(14, "W1"),
+        "mfma_plus_8_fmac_clocks_W2": clk(14, "W2"),
+        "sgpr_operand_fma_slots_W4": ratio(clk(1), fma),
+        "exp_vop3_slots_W4": ratio(clk(3), fma),
+        "scan_update_clocks_W4": clk(5),
+        "scan_update_slots_W4": ratio(clk(5), fma),
+        "mfma_32x32x16_clocks_W4": clk(4),
+        "slots_per_update_used_by_prefill_line": SLOTS_PER_UPDATE,
+    }
+    print(json.dumps({"metric": "issue clocks per wave64 instruction per SIMD", "unit": "clocks",
+                      "n_gpus": 1, "data": "synthetic", "config": {"workload": "valu_issue",
+                      "compute_units": n_cu, "waves_per_simd": [1, 2, 4, 8]},
+                      "shader_clock_GHz": round(float(np.median(clock_ghz)), 3),
+                      "results": res, "derived": derived}), flush=True)
+
+
 def att_ends_before(x, P, o):
     if x <= 0:
         return 0
@@ -627,6 +738,8 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     if args.workload == "copy":
         bench_copy(args)
+    elif args.workload == "valu_issue":
+        bench_valu_issue(args)
     elif args.workload == "proj_bf16":
         bench_proj(args)
     elif args.workload == "layer_bf16":

@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattamba.so")
+# the issue-rate microbenchmark behind the instruction-issue rooflines (not part of libattamba)
+PROBE_SRC = "issue_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libattamba_probe.so")
 SOURCES = ["boundaries.hip", "kvssm_scan.hip", "chunk_attn.hip", "attn_mfma.hip", "decode.hip", "proj_gemm.hip",
            "kvssm_scan_bwd.hip", "chunk_attn_bwd.hip", "attn_mfma_bwd.hip", "abi.hip"]
 ARCH = "gfx950"
@@ -56,11 +59,14 @@ def build(verbose: bool = False) -> str:
         src, obj = pair
         return _run([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        logs = list(ex.map(compile_one, zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
-    logs.append(_run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]))
-    os.replace(tmp, LIB)
+    probe_obj = os.path.join(BUILD, PROBE_SRC.replace(".hip", ".o"))
+    jobs = list(zip(SOURCES, objs)) + [(PROBE_SRC, probe_obj)]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        logs = list(ex.map(compile_one, jobs))
+    for lib, lib_objs in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+        tmp = lib + ".tmp"
+        logs.append(_run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *lib_objs]))
+        os.replace(tmp, lib)
     if verbose:
         for l in logs:
             if l.strip():

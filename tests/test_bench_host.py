@@ -67,3 +67,23 @@ def test_multi_gpu_request_exits():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_probe_per_simd_groups_waves_by_simd():
+    """The issue-rate probe's host arithmetic: waves are grouped by (XCC, HW_ID bits 4..15), only
+    SIMDs holding exactly W overlapping waves count, and a SIMD's clocks per instruction is its
+    busy span over the instructions its waves issued."""
+    W, ops = 2, 1000
+    rows = []
+    # SIMD A (xcc 0, simd 1): two overlapping waves spanning 100..4500 -> 4400 / 2000 = 2.2
+    rows += [[100, 4300, 0, 10, (1 << 4) | 3, 0], [200, 4500, 1, 11, (1 << 4) | 5, 0]]
+    # SIMD B (xcc 1, same HW_ID fields): overlapping, span 0..8000 -> 4.0
+    rows += [[0, 8000, 0, 10, 1 << 4, 1], [10, 7990, 0, 10, 1 << 4, 1]]
+    # SIMD C: two waves one after the other (not side by side) -> ignored
+    rows += [[0, 100, 0, 1, 2 << 4, 0], [200, 300, 2, 3, 2 << 4, 0]]
+    # SIMD D: a single wave -> ignored
+    rows += [[0, 100, 0, 1, 3 << 4, 0]]
+    r = bench.probe_per_simd(np.array(rows), ops, W)
+    assert r["simds_used"] == 2
+    assert r["clocks_per_instr_per_simd"] == pytest.approx((2.2 + 4.0) / 2)
+    assert r["waves_per_simd_histogram"] == {"1": 1, "2": 3}
