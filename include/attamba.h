@@ -249,6 +249,23 @@ int attamba_decode_workspace_size(const attamba_decode_cache* cache, size_t* byt
 int attamba_decode_step(attamba_decode_cache* cache, const attamba_decode_inputs* in,
                         attamba_stream_t stream);
 
+/* The same decode step for callers that cannot allocate device memory or be handed a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). Its
+ * scratch (the split partials of the attention) is a static device array of
+ * ATTAMBA_DECODE_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends; cache->workspace and cache->workspace_bytes are ignored. Nothing is allocated and no
+ * allocating routine is called: the first call on a device looks up the array's device address
+ * once (hipGetSymbolAddress). Nothing in the scratch needs to start at zero: every partial the
+ * step reads was written by the same step. All calls on one GPU share the one array, so calls
+ * that overlap on a GPU (on different streams, or from several threads without ordering) race
+ * and give wrong results; calls ordered on one stream are safe. Arguments, semantics and errors
+ * are those of attamba_decode_step, plus CAPACITY when the step needs more scratch than
+ * ATTAMBA_DECODE_SCRATCH_BYTES (4 * B * H * (hd + 2) * (ceil((cap + L) / 256) + 1) bytes, the
+ * size attamba_decode_workspace_size reports), and HIP if the array's address cannot be found. */
+#define ATTAMBA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int attamba_decode_step_noalloc(attamba_decode_cache* cache, const attamba_decode_inputs* in,
+                                attamba_stream_t stream);
+
 /* Prefill -> decode hand-off (pith.science "Core claim": at inference only the boundary states
  * are cached; a model serves a prompt by prefilling it and then decoding). A batch of S = B
  * sequences, each of exactly n0 tokens, was prefilled with uniform chunking of the cache's P

@@ -18,6 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattamba.so")
 
 OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_BAD_DTYPE, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_HIP = range(7)
+# bytes of the static device scratch of attamba_decode_step_noalloc (ATTAMBA_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 32 << 20
 FP32, BF16 = 0, 1
 MASK_TRAIN, MASK_TEST = 0, 1
 
@@ -99,6 +101,8 @@ EXPORTS = {
                                       C.c_int),
     "attamba_decode_step": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodeInputsStruct), _vp],
                             C.c_int),
+    "attamba_decode_step_noalloc": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodeInputsStruct),
+                                     _vp], C.c_int),
     "attamba_decode_load_prefix": ([C.POINTER(DecodeCacheStruct), C.POINTER(DecodePrefixStruct), _vp],
                                    C.c_int),
     "attamba_chunk_attn_bwd": ([C.POINTER(AttnBwdArgs), _vp], C.c_int),
@@ -484,10 +488,14 @@ class DecodeCache:
 
 
 def decode_step(cache: DecodeCache, q, x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, out=None,
-                stream=None):
-    """One generated token for every sequence. q: [B, H, hd]; x, dt_*: [B, d]; bm/cm: [B, N]."""
+                stream=None, noalloc: bool = False):
+    """One generated token for every sequence. q: [B, H, hd]; x, dt_*: [B, d]; bm/cm: [B, N].
+    noalloc: call attamba_decode_step_noalloc, whose scratch is the library's static device
+    array (the cache's workspace is not used); out must then be given."""
     B, d, N, act = cache.B, cache.d, cache.N, cache.dtype
     if out is None:
+        if noalloc:
+            raise ValueError("decode_step(noalloc=True) needs a preallocated out")
         out = torch.empty((B, cache.H, cache.hd), dtype=act, device=q.device)
     i = DecodeInputsStruct()
     i.q = _dev(q, "q", act, B * d)
@@ -499,5 +507,6 @@ def decode_step(cache: DecodeCache, q, x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, ou
     i.bm_v = _dev(bm_v, "bm_v", act, B * N)
     i.cm_v = _dev(cm_v, "cm_v", act, B * N)
     i.out = _dev(out, "out", act, B * d)
-    _check(lib().attamba_decode_step(C.byref(cache.struct), C.byref(i), _stream(stream)))
+    fn = lib().attamba_decode_step_noalloc if noalloc else lib().attamba_decode_step
+    _check(fn(C.byref(cache.struct), C.byref(i), _stream(stream)))
     return out

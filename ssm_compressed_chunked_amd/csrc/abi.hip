@@ -347,34 +347,41 @@ int attamba_decode_load_prefix(attamba_decode_cache* c, const attamba_decode_pre
   return ATTAMBA_OK;
 }
 
-int attamba_decode_step(attamba_decode_cache* c, const attamba_decode_inputs* in,
-                        attamba_stream_t stream) {
-  if (!c || !in) return fail(ATTAMBA_ERR_NULL_ARG, "decode_step: null pointer");
-  if (!dtype_ok(c->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "decode_step: dtype %d", c->dtype);
+// Checks of a decode step and its launch. Scratch: the caller's workspace (attamba_decode_step), or,
+// with static_scratch, the library's static device array, whose address is looked up only after
+// every check has passed (attamba_decode_step_noalloc).
+static int decode_step_impl(attamba_decode_cache* c, const attamba_decode_inputs* in, bool static_scratch,
+                            attamba_stream_t stream, const char* name) {
+  if (!c || !in) return fail(ATTAMBA_ERR_NULL_ARG, "%s: null pointer", name);
+  void* workspace = static_scratch ? nullptr : c->workspace;
+  const size_t workspace_bytes = static_scratch ? attamba::kDecodeScratchBytes : c->workspace_bytes;
+  if (!dtype_ok(c->dtype)) return fail(ATTAMBA_ERR_BAD_DTYPE, "%s: dtype %d", name, c->dtype);
   if (c->B < 1 || c->H < 1 || c->P < 1 || c->L < 0 || c->layer_idx < 0 || c->cap < 0 || c->pos < 0 ||
       c->n_bound < 0 || c->d != c->H * c->hd)
-    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_step: B=%d H=%d hd=%d d=%d P=%d L=%d cap=%d pos=%lld", c->B, c->H,
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "%s: B=%d H=%d hd=%d d=%d P=%d L=%d cap=%d pos=%lld", name, c->B, c->H,
                 c->hd, c->d, c->P, c->L, c->cap, static_cast<long long>(c->pos));
   if (c->hd != 32 && c->hd != 64 && c->hd != 128)
-    return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_step: hd=%d (32, 64 or 128)", c->hd);
-  if (c->N != 16 && c->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_step: N=%d (16 or 32)", c->N);
-  if (c->d % 64 != 0) return fail(ATTAMBA_ERR_UNSUPPORTED, "decode_step: d=%d not a multiple of 64", c->d);
+    return fail(ATTAMBA_ERR_UNSUPPORTED, "%s: hd=%d (32, 64 or 128)", name, c->hd);
+  if (c->N != 16 && c->N != 32) return fail(ATTAMBA_ERR_UNSUPPORTED, "%s: N=%d (16 or 32)", name, c->N);
+  if (c->d % 64 != 0) return fail(ATTAMBA_ERR_UNSUPPORTED, "%s: d=%d not a multiple of 64", name, c->d);
   if (!c->kb || !c->vb || !c->h_k || !c->h_v || !c->A_k || !c->A_v || !c->D_k || !c->D_v || !c->bias_k ||
-      !c->bias_v || !c->workspace || (c->L > 0 && (!c->kw || !c->vw)) || !in->q || !in->x || !in->dt_k ||
+      !c->bias_v || (!static_scratch && !workspace) || (c->L > 0 && (!c->kw || !c->vw)) || !in->q || !in->x || !in->dt_k ||
       !in->dt_v || !in->bm_k || !in->cm_k || !in->bm_v || !in->cm_v || !in->out)
-    return fail(ATTAMBA_ERR_NULL_ARG, "decode_step: a required pointer is null");
+    return fail(ATTAMBA_ERR_NULL_ARG, "%s: a required pointer is null", name);
   const int64_t P = c->P, o = c->layer_idx % c->P, pos = c->pos;
   if (ends_before(pos, P, o) != c->n_bound)
-    return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_step: n_bound=%d but %lld chunk ends precede pos=%lld", c->n_bound,
+    return fail(ATTAMBA_ERR_BAD_SHAPE, "%s: n_bound=%d but %lld chunk ends precede pos=%lld", name, c->n_bound,
                 static_cast<long long>(ends_before(pos, P, o)), static_cast<long long>(pos));
   attamba::DecodeLaunch dl{};
   dl.pos = pos;
   dl.is_start = starts_chunk(pos, P, o) ? 1 : 0;
   dl.is_end = starts_chunk(pos + 1, P, o) ? 1 : 0;
   if (dl.is_end && c->n_bound >= c->cap)
-    return fail(ATTAMBA_ERR_CAPACITY, "decode_step: boundary cache full (cap=%d)", c->cap);
-  if (c->workspace_bytes < attamba::decode_workspace_bytes(c->B, c->H, c->hd, c->cap, c->L))
-    return fail(ATTAMBA_ERR_CAPACITY, "decode_step: workspace of %zu bytes is too small", c->workspace_bytes);
+    return fail(ATTAMBA_ERR_CAPACITY, "%s: boundary cache full (cap=%d)", name, c->cap);
+  const size_t need = attamba::decode_workspace_bytes(c->B, c->H, c->hd, c->cap, c->L);
+  if (workspace_bytes < need)
+    return fail(ATTAMBA_ERR_CAPACITY, "%s: the step needs %zu bytes of scratch, %zu available", name, need,
+                workspace_bytes);
   dl.slot = c->L > 0 ? static_cast<int>(pos % c->L) : 0;
   dl.n_bound_before = c->n_bound;
   const int64_t w = c->L > 0 ? (pos - c->L + 1 > 0 ? pos - c->L + 1 : 0) : pos + 1;
@@ -383,13 +390,31 @@ int attamba_decode_step(attamba_decode_cache* c, const attamba_decode_inputs* in
   dl.E = static_cast<int>(ends_before(w, P, o));
   dl.n_window = c->L > 0 ? static_cast<int>(pos - w + 1) : 0;
   dl.scale = 1.0f / std::sqrt(static_cast<float>(c->hd));
-  if (pos > INT32_MAX - 2) return fail(ATTAMBA_ERR_BAD_SHAPE, "decode_step: pos too large");
-  const int st = hip_status(attamba::launch_decode_step(*c, *in, dl, reinterpret_cast<hipStream_t>(stream)),
-                            "decode_step launch");
+  if (pos > INT32_MAX - 2) return fail(ATTAMBA_ERR_BAD_SHAPE, "%s: pos too large", name);
+  if (static_scratch) {
+    const hipError_t e = attamba::decode_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(ATTAMBA_ERR_HIP, "%s: device address of the scratch: %s", name, hipGetErrorString(e));
+  }
+  attamba_decode_cache cl = *c;
+  cl.workspace = workspace;
+  cl.workspace_bytes = workspace_bytes;
+  const int st = hip_status(attamba::launch_decode_step(cl, *in, dl, reinterpret_cast<hipStream_t>(stream)),
+                            name);
   if (st != ATTAMBA_OK) return st;
   c->pos = pos + 1;
   c->n_bound += dl.is_end;
   return ATTAMBA_OK;
+}
+
+int attamba_decode_step(attamba_decode_cache* c, const attamba_decode_inputs* in,
+                        attamba_stream_t stream) {
+  return decode_step_impl(c, in, false, stream, "decode_step");
+}
+
+int attamba_decode_step_noalloc(attamba_decode_cache* c, const attamba_decode_inputs* in,
+                                attamba_stream_t stream) {
+  return decode_step_impl(c, in, true, stream, "decode_step_noalloc");
 }
 
 }  // extern "C"

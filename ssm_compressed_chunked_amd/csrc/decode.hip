@@ -13,6 +13,8 @@
 //      whole rows) and leaves an unnormalised partial (o, running max, sum) in the workspace;
 //   3. decode_combine: merges the partials of every (sequence, head).
 // The step is bound by HBM: the boundary cache is read once per step.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -383,6 +385,35 @@ hipError_t launch_decode_load_prefix(const attamba_decode_cache& c, const attamb
 }
 
 int decode_max_splits(int cap, int L) { return ceil_div(cap + L, kSplit) + 1; }
+
+// Scratch of the decode step variant that allocates nothing: the split partials live in this
+// file-scope device array instead of a caller workspace. Every GPU the library runs on holds its
+// own copy until the process ends. In host code `scratch` names a host-side stand-in, not device
+// memory, so its device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and only that address is ever passed to kernels.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L) {
   return static_cast<size_t>(B) * H * decode_max_splits(cap, L) * (hd + 2) * sizeof(float);

@@ -101,6 +101,10 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdParams& p, int hd, hipStream_t stre
 
 int decode_max_splits(int cap, int L);
 size_t decode_workspace_bytes(int B, int H, int hd, int cap, int L);
+// Size of the decode step's static device scratch (the variant that allocates nothing), and
+// its device address on the current device (looked up on first use per device).
+constexpr size_t kDecodeScratchBytes = ATTAMBA_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_decode_step(const attamba_decode_cache& c, const attamba_decode_inputs& in,
                               const DecodeLaunch& dl, hipStream_t stream);
 hipError_t launch_decode_load_prefix(const attamba_decode_cache& c, const attamba_decode_prefix& pf,

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_and_exports_agree():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert set(names) == set(B.EXPORTS), (set(names) ^ set(B.EXPORTS))
     lib = att.lib()
     for n in names:
@@ -100,6 +100,30 @@ def test_device_entry_points_validate_before_launch():
     assert lib.attamba_decode_step(C.byref(c), C.byref(i), None) == B.ERR_BAD_SHAPE
     c.d, c.hd, c.H = 96, 48, 2
     assert lib.attamba_decode_step(C.byref(c), C.byref(i), None) == B.ERR_UNSUPPORTED
+    # the variant with the library's static scratch checks its pointers before anything else
+    assert lib.attamba_decode_step_noalloc(None, C.byref(i), None) == B.ERR_NULL_ARG
+    assert lib.attamba_decode_step_noalloc(C.byref(c), None, None) == B.ERR_NULL_ARG
+
+
+def test_decode_noalloc_rejects_steps_beyond_its_scratch():
+    """attamba_decode_step_noalloc fails with CAPACITY, on the host and before looking up or
+    touching any device memory, when the step's split partials (4 B H (hd + 2) (ceil((cap + L) /
+    256) + 1) bytes) exceed ATTAMBA_DECODE_SCRATCH_BYTES; the pointers are never dereferenced."""
+    lib = att.lib()
+    c = B.DecodeCacheStruct()
+    c.B, c.H, c.hd, c.d, c.N, c.P, c.L, c.layer_idx, c.dtype = 64, 32, 128, 4096, 16, 4, 256, 0, 1
+    c.pos, c.n_bound = 32768, 8192
+    c.cap = 8192 + 4
+    for f in ("kb", "vb", "kw", "vw", "h_k", "h_v", "A_k", "A_v", "D_k", "D_v", "bias_k", "bias_v"):
+        setattr(c, f, 4096)           # placeholders: the size check fails first
+    i = B.DecodeInputsStruct()
+    for f in ("q", "x", "dt_k", "dt_v", "bm_k", "cm_k", "bm_v", "cm_v", "out"):
+        setattr(i, f, 4096)
+    need = 4 * c.B * c.H * (c.hd + 2) * (-(-(c.cap + c.L) // 256) + 1)
+    assert need > B.DECODE_SCRATCH_BYTES
+    assert lib.attamba_decode_step_noalloc(C.byref(c), C.byref(i), None) == B.ERR_CAPACITY
+    assert b"scratch" in lib.attamba_last_error()
+    assert c.pos == 32768 and c.n_bound == 8192     # unchanged on error
 
 
 def test_input_proj_validates_before_launch():
@@ -218,3 +242,10 @@ def test_decode_load_prefix_validates_before_launch():
     pf.h_last_v = fake
     c.hd, c.d = 48, 96
     assert lib.attamba_decode_load_prefix(C.byref(c), C.byref(pf), None) == B.ERR_UNSUPPORTED
+
+
+def test_decode_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTAMBA_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "ATTAMBA_DECODE_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == B.DECODE_SCRATCH_BYTES
