@@ -201,6 +201,54 @@ def selective_scan_backward(x, dt, dt_bias, A, Bm, Cm, D, chunk_cu, gy):
     return g
 
 
+# ----------------------------------------------------------------------------------------
+# Mamba-block variant of the KV-SSM. The selective SSM is the core of a Mamba block
+# (pith.science "Assumptions & free parameters": selective state-space models, Mamba, Section
+# 3.2, Eq. 3). Around the scan, a Mamba block puts a short causal depthwise convolution followed
+# by SiLU on the scan's input, and multiplies the scan's output by SiLU of a second projection
+# of the layer input (the gate). The block runs on each chunk on its own ("Core claim": K^(p) =
+# SSM_K(X^(p)) per chunk), so the convolution restarts at every chunk start, as the state does:
+# positions before the chunk start count as zero.
+# ----------------------------------------------------------------------------------------
+def silu(v):
+    """SiLU: v * sigmoid(v) = v / (1 + exp(-v))."""
+    v = np.asarray(v, np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+def chunk_causal_conv(x, w, b, chunk_cu):
+    """Depthwise causal convolution that restarts at every chunk:
+    out[t, c] = b[c] + sum_k w[c, k] * x[t - (K - 1) + k, c], where positions before the start
+    of t's chunk count as zero. x: [T, d]; w: [d, K] (tap K - 1 multiplies the current token);
+    b: [d]. Returns float64 [T, d]."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    b = np.asarray(b, np.float64)
+    T, d = x.shape
+    K = w.shape[1]
+    out = np.empty((T, d))
+    cu = [int(v) for v in chunk_cu]
+    for a, e in zip(cu[:-1], cu[1:]):
+        for t in range(a, e):
+            acc = b.copy()
+            for k in range(K):
+                s = t - (K - 1) + k
+                if s >= a:
+                    acc = acc + w[:, k] * x[s]
+            out[t] = acc
+    return out
+
+
+def ssm_block_scan(x, dt, dt_bias, A, Bm, Cm, D, chunk_cu, conv_w=None, conv_b=None, z=None):
+    """The scan of one SSM inside a Mamba block, chunk by chunk: xc = silu(conv(x)) when conv_w
+    is given (else xc = x); y = selective_scan(xc, ...), whose skip term D * xc uses the scan's
+    own input; out = y * silu(z) when the gate input z [T, d] is given (else out = y).
+    Returns out [T, d]; its value at a chunk's last token is the chunk's boundary state."""
+    xc = x if conv_w is None else silu(chunk_causal_conv(x, conv_w, conv_b, chunk_cu))
+    y, _ = selective_scan(xc, dt, dt_bias, A, Bm, Cm, D, chunk_cu)
+    return y if z is None else y * silu(z)
+
+
 def boundary_states(y, chunk_cu):
     """One state per chunk: the SSM output y at the chunk's last token (pith.science review,
     Referee Report, comment on Eq. 7: the boundary state K^(p)[-1] is the output once the

@@ -12,7 +12,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "attamba_oracle.py")
 PINS = ["test_oracle_segment.py", "test_oracle_scan.py", "test_oracle_attention.py",
-        "test_oracle_decode.py", "test_oracle_proj.py", "test_oracle_backward.py"]
+        "test_oracle_decode.py", "test_oracle_proj.py", "test_oracle_backward.py",
+        "test_oracle_block.py"]
 
 MUTANTS = [
     ("decay uses the previous step size", "decay = np.exp(delta[k][:, None] * A)",
@@ -59,6 +60,13 @@ MUTANTS = [
      "g[\"dA\"] += de * e"),
     ("backward key gradient from dS instead of dS^T", "dk[:, h, :] = scale * (ds.T @ q[:, h, :])",
      "dk[:, h, :] = scale * (ds @ q[:, h, :])"),
+    ("convolution taps reversed", "acc = acc + w[:, k] * x[s]", "acc = acc + w[:, K - 1 - k] * x[s]"),
+    ("convolution does not restart at chunk starts", "                if s >= a:\n", "                if s >= 0:\n"),
+    ("convolution bias dropped", "            acc = b.copy()", "            acc = np.zeros(d)"),
+    ("SiLU replaced by the logistic function", "return v / (1.0 + np.exp(-v))", "return 1.0 / (1.0 + np.exp(-v))"),
+    ("gate applied without SiLU", "return y if z is None else y * silu(z)", "return y if z is None else y * z"),
+    ("block skip term on the raw input", "    y, _ = selective_scan(xc, dt, dt_bias, A, Bm, Cm, D, chunk_cu)\n    return y if z",
+     "    y, _ = selective_scan(xc, dt, dt_bias, A, Bm, Cm, D, chunk_cu)\n    y = y + D * (np.asarray(x) - xc)\n    return y if z"),
 ]
 
 
