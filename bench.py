@@ -14,6 +14,7 @@ train_bf16 forward's working set fits in the 256 MB MALL, so both are reported).
     python bench.py --workload train_step_bf16  # forward + backward at the M_train workload
     python bench.py --workload copy             # reference bandwidth (512 MiB device copy)
     python bench.py --workload valu_issue       # clocks per wave64 VALU / MFMA instruction
+    python bench.py --workload block_bf16       # prefill_bf16 with the Mamba-block pieces
 """
 from __future__ import annotations
 
@@ -159,11 +160,18 @@ def bench_prefill(args):
     from ssm_compressed_chunked_amd.pipeline import chunk_layout
     from workloads import PREFILL_CONFIGS, make_prefill
 
-    cfg = PREFILL_CONFIGS[args.workload]
+    # block_bf16: the prefill workload with the Mamba-block pieces around both SSMs (a 4-tap
+    # causal convolution with SiLU on their input, a SiLU gate on their output)
+    with_block = args.workload == "block_bf16"
+    cfg = PREFILL_CONFIGS["prefill_bf16" if with_block else args.workload]
     inp = make_prefill(cfg)
     dev = torch.device("cuda", 0)
     act = {k: v.to(dev) for k, v in inp.act.items()}
     par = {k: v.to(dev) for k, v in inp.param.items()}
+    block = None
+    if with_block:
+        from workloads import make_block_inputs
+        block = {k: v.to(dev) for k, v in make_block_inputs(inp, 4, seed=cfg.seed).items()}
     seq_cu = torch.from_numpy(inp.seq_cu).to(dev)
     T, d, H, hd = cfg.T, cfg.d, cfg.H, cfg.hd
     rnd = cfg.chunking == "random"
@@ -199,7 +207,8 @@ def bench_prefill(args):
             ev[1].record(stream)
         att.kvssm_scan(act["x"], act["dt_k"], act["dt_v"], act["bm_k"], act["cm_k"], act["bm_v"],
                        act["cm_v"], par["A_k"], par["A_v"], par["D_k"], par["D_v"], par["bias_k"],
-                       par["bias_v"], chunk_cu, y_k=y_k, y_v=y_v, kb=kb, vb=vb, stream=stream)
+                       par["bias_v"], chunk_cu, y_k=y_k, y_v=y_v, kb=kb, vb=vb, block=block,
+                       stream=stream)
         if ev is not None:
             ev[2].record(stream)
         att.chunk_attn_fwd(act["q"].view(T, H, hd), y_k.view(T, H, hd), y_v.view(T, H, hd),
@@ -244,13 +253,14 @@ def bench_prefill(args):
                             cfg.L, mode == att.MASK_TRAIN)
     attn_flop = 4.0 * hd * H * pairs
     attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
-    scan_bytes = scan_algorithmic_bytes(cfg)
+    scan_bytes = scan_algorithmic_bytes(cfg) + (2 * T * d * 2 if with_block else 0)   # + z_k, z_v
     scan_gbps = scan_bytes / (scan_ms * 1e-3) / 1e9
     updates = 2 * T * d * cfg.N
     scan_slots = SLOTS_PER_UPDATE * updates
     scan_alu_tslots = scan_slots / (scan_ms * 1e-3) / 1e12
     alu_peak = VALU_SLOTS_PER_S / 1e12
-    traffic = measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"], args.workload)
+    traffic = None if with_block else measured_traffic("kvssm_scan_kernel", ["kvssm_scan.hip", "common.h"],
+                                                       args.workload)
     attn_traffic = measured_traffic("attn_mfma_kernel", ["attn_mfma.hip", "attn_geom.h", "attn_tiles.h",
                                                          "common.h"], args.workload)
     # The scan is the dominant kernel; its roofline is HBM: algorithmic bytes per launch over
@@ -269,7 +279,7 @@ def bench_prefill(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02^2), projections computed)",
-        "config": {"workload": cfg.name, "B": cfg.B, "n": cfg.n, "d_model": d, "heads": H,
+        "config": {"workload": args.workload if with_block else cfg.name, "B": cfg.B, "n": cfg.n, "d_model": d, "heads": H,
                    "head_dim": hd, "N": cfg.N, "P": cfg.P, "L": cfg.L, "layer_idx": cfg.layer_idx,
                    "mask": "M_train+window" if mode == att.MASK_TRAIN else "M_test+window",
                    "chunking": cfg.chunking, "n_chunks": n},
@@ -283,7 +293,7 @@ def bench_prefill(args):
                       "frac_of_2.5PF": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                       "traffic": None if attn_traffic is None else attn_traffic["bytes_per_launch"]},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not with_block:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, T)
     print(json.dumps(line), flush=True)
 

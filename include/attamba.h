@@ -117,6 +117,24 @@ int attamba_chunk_index(const int32_t* chunk_cu, int32_t n_chunks, int32_t T,
  * projections in front of the SSMs (pith.science "If this is right": dropping them costs
  * about 1 % perplexity), x_v gives SSM_V its own input (x then feeds SSM_K only).
  * ---------------------------------------------------------------------------------------- */
+/* Optional Mamba-block pieces around each SSM (pith.science "Assumptions & free parameters":
+ * the selective SSM is the core of a Mamba block, Section 3.2, Eq. 3). With them, SSM S scans
+ *   xc = silu(conv_b_S + sum_k conv_w_S[c, k] * xin[t - (K-1) + k])     (causal, depthwise)
+ * instead of its input xin (x, or x_v for SSM_V), with the skip term D_S * xc, and its outputs
+ * become y * silu(z_S[t, c]); silu(v) = v / (1 + e^-v). The block runs on each chunk alone, so the
+ * convolution restarts at every chunk start like the state: positions before the chunk start
+ * count as zero. The boundary state of a chunk is the (gated) output at its last token.
+ * Forward only: the scan backward and the decode step take the plain SSM. */
+typedef struct {
+  int32_t conv_width;   /* taps K of the convolution, 1..4; 0: no convolution (xc = xin) */
+  const float* conv_w_k;/* [d, K] taps of SSM_K's convolution; tap K-1 weighs the current token */
+  const float* conv_b_k;/* [d] */
+  const float* conv_w_v;/* [d, K] */
+  const float* conv_b_v;/* [d] */
+  const void* z_k;      /* [T, d] gate input of SSM_K (activation dtype), or NULL: no gate */
+  const void* z_v;      /* [T, d] gate input of SSM_V, or NULL */
+} attamba_ssm_block_args;
+
 typedef struct {
   int32_t T;        /* tokens in the packed batch (>= 0) */
   int32_t d;        /* channels = H * hd; multiple of 64 */
@@ -147,9 +165,11 @@ typedef struct {
   float* h_last_k;                    /* [S, d, N] out or NULL */
   float* h_last_v;                    /* [S, d, N] out or NULL */
   const void* x_v;                    /* [T, d] input of SSM_V, or NULL: SSM_V reads x */
+  const attamba_ssm_block_args* block;/* Mamba-block convolution and gate, or NULL: plain SSMs */
 } attamba_scan_args;
 
-/* Errors: NULL_ARG, BAD_SHAPE (T, n_chunks < 0; d not a positive multiple of 64),
+/* Errors: NULL_ARG (also a block whose conv_width > 0 lacks a tap or bias array), BAD_SHAPE
+ * (T, n_chunks < 0; d not a positive multiple of 64; block conv_width outside 0..4),
  * BAD_DTYPE, UNSUPPORTED (N not 16 or 32, or T*d of 2^31 elements or more), HIP. */
 int attamba_kvssm_scan(const attamba_scan_args* args, attamba_stream_t stream);
 
@@ -370,7 +390,7 @@ int attamba_chunk_attn_bwd(const attamba_attn_bwd_args* args, attamba_stream_t s
 int attamba_chunk_attn_bwd_workspace_size(const attamba_attn_bwd_args* args, size_t* elems);
 
 /* KV-SSM scan backward. fwd holds the forward call's arguments (only its inputs are read; its
- * outputs may be NULL). Given the gradients of y_k, y_v (and optionally of kb, vb, added at each
+ * outputs may be NULL; fwd.block must be NULL: UNSUPPORTED otherwise). Given the gradients of y_k, y_v (and optionally of kb, vb, added at each
  * chunk's last token), writes per SSM S in {K, V}:
  *   dx_S   gradient of S's input through S (x for SSM_K; x_v, or x when x_v is NULL, for SSM_V):
  *          when both SSMs read x, the gradient of x is dx_k + dx_v;

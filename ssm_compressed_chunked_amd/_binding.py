@@ -28,13 +28,19 @@ _i32 = C.c_int32
 _i32p = C.POINTER(C.c_int32)
 
 
+class SsmBlockArgs(C.Structure):
+    _fields_ = [("conv_width", _i32), ("conv_w_k", _vp), ("conv_b_k", _vp), ("conv_w_v", _vp),
+                ("conv_b_v", _vp), ("z_k", _vp), ("z_v", _vp)]
+
+
 class ScanArgs(C.Structure):
     _fields_ = [("T", _i32), ("d", _i32), ("N", _i32), ("dtype", _i32), ("n_chunks", _i32),
                 ("chunk_cu", _vp), ("x", _vp), ("dt_k", _vp), ("dt_v", _vp), ("bm_k", _vp),
                 ("cm_k", _vp), ("bm_v", _vp), ("cm_v", _vp), ("A_k", _vp), ("A_v", _vp),
                 ("D_k", _vp), ("D_v", _vp), ("bias_k", _vp), ("bias_v", _vp), ("y_k", _vp),
                 ("y_v", _vp), ("kb", _vp), ("vb", _vp), ("seq_cu", _vp), ("S", _i32),
-                ("h_last_k", _vp), ("h_last_v", _vp), ("x_v", _vp)]
+                ("h_last_k", _vp), ("h_last_v", _vp), ("x_v", _vp),
+                ("block", C.POINTER(SsmBlockArgs))]
 
 
 PROJ_MAX_SEGMENTS = 12
@@ -247,9 +253,11 @@ def _scan_inputs(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias
 
 def kvssm_scan(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k, bias_v,
                chunk_cu, *, y_k=None, y_v=None, kb=None, vb=None, boundaries=True,
-               seq_cu=None, h_last=False, x_v=None, stream=None) -> dict:
+               seq_cu=None, h_last=False, x_v=None, block=None, stream=None) -> dict:
     """Both selective scans in one pass. x_v: optional separate input of SSM_V (x then feeds
-    SSM_K only). Returns dict(y_k, y_v, kb, vb, h_last_k, h_last_v)."""
+    SSM_K only). block: optional Mamba-block pieces, a dict with conv_w_k, conv_b_k, conv_w_v,
+    conv_b_v (float32 [d, K] taps and [d] biases, K <= 4) and/or z_k, z_v ([T, d] gate inputs in
+    the activation dtype). Returns dict(y_k, y_v, kb, vb, h_last_k, h_last_v)."""
     T, d = x.shape
     N = A_k.shape[1]
     n_chunks = chunk_cu.numel() - 1
@@ -278,6 +286,20 @@ def kvssm_scan(x, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v, A_k, A_v, D_k, D_v, bias_k
     a.S = S
     a.h_last_k = _dev(hk, "h_last_k")
     a.h_last_v = _dev(hv, "h_last_v")
+    if block is not None:
+        bl = SsmBlockArgs()
+        w_k = block.get("conv_w_k")
+        if w_k is not None:
+            K = w_k.shape[1]
+            bl.conv_width = K
+            for name in ("conv_w_k", "conv_w_v"):
+                setattr(bl, name, _dev(block[name], name, torch.float32, d * K))
+            for name in ("conv_b_k", "conv_b_v"):
+                setattr(bl, name, _dev(block[name], name, torch.float32, d))
+        for name in ("z_k", "z_v"):
+            if block.get(name) is not None:
+                setattr(bl, name, _dev(block[name], name, act, T * d))
+        a.block = C.pointer(bl)
     _check(lib().attamba_kvssm_scan(C.byref(a), _stream(stream)))
     return dict(y_k=y_k, y_v=y_v, kb=kb, vb=vb, h_last_k=hk, h_last_v=hv)
 

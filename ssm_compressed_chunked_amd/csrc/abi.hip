@@ -186,6 +186,13 @@ int attamba_kvssm_scan(const attamba_scan_args* a, attamba_stream_t stream) {
   if (!a->h_last_k != !a->h_last_v) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: h_last_k/h_last_v must match");
   if (a->h_last_k && (!a->seq_cu || a->S < 1))
     return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: h_last needs seq_cu and S >= 1");
+  if (const attamba_ssm_block_args* b = a->block) {
+    if (b->conv_width < 0 || b->conv_width > 4)
+      return fail(ATTAMBA_ERR_BAD_SHAPE, "kvssm_scan: block conv_width=%d (0..4)", b->conv_width);
+    if (b->conv_width > 0 && (!b->conv_w_k || !b->conv_b_k || !b->conv_w_v || !b->conv_b_v))
+      return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: block convolution taps or bias null");
+    if (!b->z_k != !b->z_v) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan: block z_k and z_v must both be set or both null");
+  }
   return hip_status(attamba::launch_kvssm_scan(*a, reinterpret_cast<hipStream_t>(stream)), "kvssm_scan launch");
 }
 
@@ -193,6 +200,7 @@ int attamba_kvssm_scan_bwd(const attamba_scan_bwd_args* b, attamba_stream_t stre
   if (!b) return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan_bwd: args null");
   const attamba_scan_args* a = &b->fwd;
   if (const int st = check_scan(a, "kvssm_scan_bwd")) return st;
+  if (a->block) return fail(ATTAMBA_ERR_UNSUPPORTED, "kvssm_scan_bwd: the Mamba-block variant has no backward");
   if (!b->gy_k || !b->gy_v || !b->dx_k || !b->dx_v || !b->ddt_k || !b->ddt_v || !b->dbm_k || !b->dcm_k ||
       !b->dbm_v || !b->dcm_v || !b->dA_k || !b->dA_v || !b->dD_k || !b->dD_v || !b->dbias_k || !b->dbias_v)
     return fail(ATTAMBA_ERR_NULL_ARG, "kvssm_scan_bwd: a required gradient pointer is null");

@@ -35,6 +35,12 @@ __device__ __forceinline__ float softplus_f32(float z) {
   return z > 20.0f ? z : r;
 }
 
+// silu(v) = v sigmoid(v) = v / (1 + e^-v), with the hardware exponential and reciprocal (each
+// within about one ulp); for v far below zero e^-v is +inf and the result is -0.
+__device__ __forceinline__ float silu_f32(float v) {
+  return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e));
+}
+
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace attamba

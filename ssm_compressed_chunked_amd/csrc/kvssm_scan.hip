@@ -22,6 +22,11 @@
 // the next chunk anyway), so no register copies are needed. Other chunk lengths (random
 // chunking, a partial first or last chunk) run in blocks of up to PU tokens with the same
 // loads up front and the same one-token row prefetch.
+// The Mamba-block variant (BLK) adds, per lane, a causal depthwise convolution of up to 4 taps
+// with SiLU on the scan's input and a SiLU gate on its output. The convolution restarts at every
+// chunk start like the state, so it needs no tokens from before the chunk: inside a block it
+// reads the block's own x registers, and across the blocks of a long chunk it carries the last
+// three inputs.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,6 +58,39 @@ struct SideArgs {
   T* y;
   T* b;                // boundary outputs or null
   float* h_last;       // hand-off states or null
+  // Mamba-block pieces (read only by the BLK instances)
+  int conv_width;      // 0: no convolution
+  const float* conv_w; // [d, conv_width]
+  const float* conv_b; // [d]
+  const T* z;          // [T, d] gate input or null
+};
+
+// The convolution taps of one lane, right-aligned in 4 slots (w4[3] weighs the current token,
+// slots before the first tap are zero), and its bias.
+struct ConvLane {
+  float w4[4];
+  float b;
+  __device__ __forceinline__ void load(const float* __restrict__ w, const float* __restrict__ bias,
+                                       int K, int c) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w4[k] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < K) w4[4 - K + k] = w[c * K + k];
+    b = bias[c];
+  }
+  // silu of the convolution at block token j, from the block's inputs xs and the three inputs
+  // before the block (prev[0] is the oldest; zero before the chunk start)
+  template <int PU>
+  __device__ __forceinline__ float at(const float (&xs)[PU], const float (&prev)[3], int j) const {
+    float acc = b;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = j - 3 + k;
+      acc = fmaf(w4[k], s >= 0 ? xs[s] : prev[3 + s], acc);
+    }
+    return silu_f32(acc);
+  }
 };
 
 // Workgroup id -> (SSM, chunk group, channel tile). Workgroups are dispatched round-robin over
@@ -145,10 +183,10 @@ __device__ __forceinline__ void rows_ready(uint32_t b0, uint32_t c0) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename T, int N, int PU, int CPW>
+template <typename T, int N, int PU, int CPW, bool BLK>
 // bf16 with N = 16 (the common case) is held to 7 waves per SIMD (72 VGPRs; the other-length
 // path would otherwise take 73 and lose a wave); the other instances are left unconstrained.
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 && sizeof(T) == 2 ? 7 : 1))) void kvssm_scan_kernel(
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 && sizeof(T) == 2 && !BLK ? 7 : 1))) void kvssm_scan_kernel(
     ScanShape sh, const int32_t* __restrict__ chunk_cu, const int32_t* __restrict__ seq_cu,
     SideArgs<T> ka, SideArgs<T> va) {
   int side, group, ctile;
@@ -167,6 +205,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
 
   SsmLane<T, N> s;
   s.load_params(a.A, a.D, a.bias, c);
+  ConvLane cv{};
+  const bool conv = BLK && a.conv_width > 0;
+  const bool gated = BLK && a.z != nullptr;
+  if (conv) cv.load(a.conv_w, a.conv_b, a.conv_width, c);
 
   // end of chunk q: boundary state and, for the last chunk of a sequence, the hand-off state
   auto chunk_end = [&](int q, int cs, int ce, float out) {
@@ -190,12 +232,21 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
     const int ce = chunk_cu[q + 1];
     float out = 0.f;
     if (ce - cs == PU) {
-      float xs[PU], dts[PU];
+      float xs[PU], dts[PU], zs[PU];
 #pragma unroll
       for (int j = 0; j < PU; ++j) {
         const int o = (cs + j) * d + c;
         xs[j] = to_f32(x[o]);
         dts[j] = to_f32(dt[o]);
+        if (gated) zs[j] = to_f32(a.z[o]);
+      }
+      if (conv) {   // the chunk starts here: nothing before it counts
+        const float prev[3] = {0.f, 0.f, 0.f};
+        float xc[PU];
+#pragma unroll
+        for (int j = 0; j < PU; ++j) xc[j] = cv.at<PU>(xs, prev, j);
+#pragma unroll
+        for (int j = 0; j < PU; ++j) xs[j] = xc[j];
       }
       typename SsmLane<T, N>::Rows rn, rc;
       SsmLane<T, N>::load_rows(bm + cs * N, cm + cs * N, rn);
@@ -208,19 +259,42 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
         order_point();
         if (j == 0) out = s.template step<true>(xs[j], dts[j], rc);
         else out = s.template step<false>(xs[j], dts[j], rc);
+        if (gated) out *= silu_f32(zs[j]);
         y[t * d + c] = from_f32<T>(out);
       }
     } else {
       // any other length: blocks of up to PU tokens, each with its x/dt loads issued up front
       // (the state runs on across the blocks of a chunk)
+      float prev[3] = {0.f, 0.f, 0.f};   // convolution inputs before the block (chunk start: 0)
       for (int bs = cs; bs < ce; bs += PU) {
         const int nb = min(PU, ce - bs);
-        float xs[PU], dts[PU];
+        float xs[PU], dts[PU], zs[PU];
 #pragma unroll
         for (int j = 0; j < PU; ++j) {   // past the block's end: its last token again (unused)
           const int o = (bs + min(j, nb - 1)) * d + c;
           xs[j] = to_f32(x[o]);
           dts[j] = to_f32(dt[o]);
+          if (gated) zs[j] = to_f32(a.z[o]);
+        }
+        if (conv) {
+          float xc[PU];
+#pragma unroll
+          for (int j = 0; j < PU; ++j) xc[j] = cv.at<PU>(xs, prev, j);
+          // the last three raw inputs up to the block's end (nb is uniform over the wave)
+          float w[PU + 3];
+#pragma unroll
+          for (int i = 0; i < 3; ++i) w[i] = prev[i];
+#pragma unroll
+          for (int j = 0; j < PU; ++j) w[3 + j] = xs[j];
+#pragma unroll
+          for (int m = 1; m <= PU; ++m)
+            if (nb == m) {
+              prev[0] = w[m];
+              prev[1] = w[m + 1];
+              prev[2] = w[m + 2];
+            }
+#pragma unroll
+          for (int j = 0; j < PU; ++j) xs[j] = xc[j];
         }
         typename SsmLane<T, N>::Rows rn, rc;
         SsmLane<T, N>::load_rows(bm + bs * N, cm + bs * N, rn);
@@ -234,6 +308,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
             order_point();
             if (j == 0 && bs == cs) out = s.template step<true>(xs[j], dts[j], rc);
             else out = s.template step<false>(xs[j], dts[j], rc);
+            if (gated) out *= silu_f32(zs[j]);
             y[t * d + c] = from_f32<T>(out);
           }
         }
@@ -244,23 +319,34 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
   }
 }
 
-template <typename T, int N>
+template <typename T, int N, bool BLK>
 hipError_t launch_typed(const attamba_scan_args& a, const ScanShape& sh, int cpw,
                         hipStream_t stream) {
   const int blocks = ceil_div(sh.groups, 8) * 8 * sh.ctiles * 2;
+  const attamba_ssm_block_args* bl = a.block;
   SideArgs<T> k{static_cast<const T*>(a.x), static_cast<const T*>(a.dt_k),
                 static_cast<const T*>(a.bm_k), static_cast<const T*>(a.cm_k), a.A_k, a.D_k,
-                a.bias_k, static_cast<T*>(a.y_k), static_cast<T*>(a.kb), a.h_last_k};
+                a.bias_k, static_cast<T*>(a.y_k), static_cast<T*>(a.kb), a.h_last_k,
+                bl ? bl->conv_width : 0, bl ? bl->conv_w_k : nullptr, bl ? bl->conv_b_k : nullptr,
+                bl ? static_cast<const T*>(bl->z_k) : nullptr};
   SideArgs<T> v{static_cast<const T*>(a.x_v ? a.x_v : a.x), static_cast<const T*>(a.dt_v),
                 static_cast<const T*>(a.bm_v), static_cast<const T*>(a.cm_v), a.A_v, a.D_v,
-                a.bias_v, static_cast<T*>(a.y_v), static_cast<T*>(a.vb), a.h_last_v};
+                a.bias_v, static_cast<T*>(a.y_v), static_cast<T*>(a.vb), a.h_last_v,
+                bl ? bl->conv_width : 0, bl ? bl->conv_w_v : nullptr, bl ? bl->conv_b_v : nullptr,
+                bl ? static_cast<const T*>(bl->z_v) : nullptr};
   if (cpw == 2)
-    hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, 2>), dim3(blocks), dim3(kWave), 0, stream, sh,
+    hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, 2, BLK>), dim3(blocks), dim3(kWave), 0, stream, sh,
                        a.chunk_cu, a.seq_cu, k, v);
   else
-    hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, 1>), dim3(blocks), dim3(kWave), 0, stream, sh,
+    hipLaunchKernelGGL((kvssm_scan_kernel<T, N, 8, 1, BLK>), dim3(blocks), dim3(kWave), 0, stream, sh,
                        a.chunk_cu, a.seq_cu, k, v);
   return hipGetLastError();
+}
+
+template <typename T, int N>
+hipError_t launch_blk(const attamba_scan_args& a, const ScanShape& sh, int cpw, hipStream_t stream) {
+  const bool blk = a.block && (a.block->conv_width > 0 || a.block->z_k);
+  return blk ? launch_typed<T, N, true>(a, sh, cpw, stream) : launch_typed<T, N, false>(a, sh, cpw, stream);
 }
 
 }  // namespace
@@ -274,8 +360,8 @@ hipError_t launch_kvssm_scan(const attamba_scan_args& a, hipStream_t stream) {
   const int cpw = waves2 >= static_cast<long>(kRoundsForTwoChunks) * kResidentWaves ? 2 : 1;
   sh.groups = ceil_div(a.n_chunks, cpw);
   if (a.dtype == ATTAMBA_BF16)
-    return a.N == 16 ? launch_typed<__bf16, 16>(a, sh, cpw, stream) : launch_typed<__bf16, 32>(a, sh, cpw, stream);
-  return a.N == 16 ? launch_typed<float, 16>(a, sh, cpw, stream) : launch_typed<float, 32>(a, sh, cpw, stream);
+    return a.N == 16 ? launch_blk<__bf16, 16>(a, sh, cpw, stream) : launch_blk<__bf16, 32>(a, sh, cpw, stream);
+  return a.N == 16 ? launch_blk<float, 16>(a, sh, cpw, stream) : launch_blk<float, 32>(a, sh, cpw, stream);
 }
 
 }  // namespace attamba

@@ -36,10 +36,12 @@ def chunk_layout(seq_cu_host, seq_cu: torch.Tensor, T: int, P: int | None, layer
 
 def prefill_forward(act: dict, params: dict, seq_cu_host, H: int, hd: int, P: int | None,
                     layer_idx: int, L: int, mode: int, chunk_lens=None, layout=None,
-                    stream=None, want_lse: bool = True, h_last: bool = False) -> dict:
+                    stream=None, want_lse: bool = True, h_last: bool = False,
+                    block: dict | None = None) -> dict:
     """act: device tensors x, q, dt_k, dt_v, bm_k, cm_k, bm_v, cm_v; params: A_k, A_v, D_k,
     D_v, bias_k, bias_v (float32). Returns the layout, the scan outputs and (out, lse).
-    h_last: also return the SSM states after each sequence's last token (decode hand-off)."""
+    h_last: also return the SSM states after each sequence's last token (decode hand-off).
+    block: the Mamba-block variant's convolution taps/biases and gate inputs (see kvssm_scan)."""
     x = act["x"]
     T, d = x.shape
     seq_cu_host = np.asarray(seq_cu_host, dtype=np.int32)
@@ -52,7 +54,7 @@ def prefill_forward(act: dict, params: dict, seq_cu_host, H: int, hd: int, P: in
                         act["bm_v"], act["cm_v"], params["A_k"], params["A_v"], params["D_k"],
                         params["D_v"], params["bias_k"], params["bias_v"], layout.chunk_cu,
                         x_v=act.get("x_v"), seq_cu=seq_cu if h_last else None, h_last=h_last,
-                        stream=stream)
+                        block=block, stream=stream)
     max_len = int(np.max(np.diff(seq_cu_host))) if len(seq_cu_host) > 1 else 0
     n = layout.n_chunks
     out, lse = B.chunk_attn_fwd(act["q"].view(T, H, hd), scan["y_k"].view(T, H, hd),

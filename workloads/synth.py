@@ -116,6 +116,27 @@ def make_ragged_prefill(base: PrefillConfig, lengths: list[int], seed: int,
     return PrefillInputs(cfg=cfg, seq_cu=seq_cu, chunk_lens=cl, act=act, param=params)
 
 
+def make_block_inputs(inp: PrefillInputs, K: int, seed: int, gate: bool = True) -> dict:
+    """Seeded parameters and inputs of the Mamba-block pieces around both SSMs: depthwise
+    convolution taps [d, K] and biases [d] drawn U(-1/sqrt(K), 1/sqrt(K)) (the default
+    initialisation of a depthwise convolution, fan-in K), float32; and, if gate, the gate inputs
+    z_k, z_v = x W_z with W_z ~ N(0, 0.02^2) like the other projections, computed in float32
+    from the stored x and rounded to the activation type. Returns a dict of CPU tensors."""
+    rng = np.random.default_rng((seed, 4))
+    d = inp.cfg.d
+    lim = 1.0 / np.sqrt(K)
+    out = {}
+    for s in ("k", "v"):
+        out[f"conv_w_{s}"] = torch.from_numpy(rng.uniform(-lim, lim, (d, K)).astype(np.float32))
+        out[f"conv_b_{s}"] = torch.from_numpy(rng.uniform(-lim, lim, d).astype(np.float32))
+    if gate:
+        x32 = inp.act["x"].to(torch.float32).numpy()
+        for s in ("k", "v"):
+            wz = rng.standard_normal((d, d), dtype=np.float32) * np.float32(0.02)
+            out[f"z_{s}"] = torch.from_numpy(x32 @ wz).to(inp.act["x"].dtype)
+    return out
+
+
 @dataclass
 class ProjInputs:
     """Layer input x [T, d] and the stacked projection weight w [n_out, d] (one row per
