@@ -9,4 +9,5 @@ from .attamba_oracle import (TEST, TRAIN, DecodeSeq, boundary_states, chunk_atte
                              decode_state_from_prefix, decode_step, dense_mask,
                              is_chunk_end_at, is_chunk_start_at, kvssm_forward, linear,
                              masked_attention, segment, selective_scan, softplus,
-                             uniform_chunk_starts, silu, chunk_causal_conv, ssm_block_scan)
+                             uniform_chunk_starts, silu, chunk_causal_conv, ssm_block_scan,
+                             round_to_bf16, stack_forward)

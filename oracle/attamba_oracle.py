@@ -403,6 +403,45 @@ def kvssm_forward(inp: dict, seq_cu, H: int, hd: int, P: int | None, layer_idx: 
 
 
 # ----------------------------------------------------------------------------------------
+# A stack of layers (pith.science "What carries the argument": cyclic chunking shifts the chunk
+# offset by layer index). Layer l uses layer index first_layer + l; its attention output is the
+# next layer's input (the output projection, MLP and norms between attention layers are outside
+# the path). The path stores what one call hands to the next in bf16, so the chain rounds the
+# projections and each layer's output to bf16 (round to nearest, ties to even) where the next
+# call reads them.
+# ----------------------------------------------------------------------------------------
+def round_to_bf16(a):
+    """a rounded to the nearest bf16 value (8 significant bits), ties to even; float64 out."""
+    a = np.asarray(a, np.float64)
+    m, e = np.frexp(a)                   # a = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0), e - 8)
+
+
+def stack_forward(x, layers, seq_cu, H: int, hd: int, N: int, P: int, L: int, mode: str,
+                  first_layer: int = 0):
+    """x [T, d] (layer 0's input); layers[l] = dict(w [3 d + 4 N, d], params) with params A_k,
+    A_v, D_k, D_v, bias_k, bias_v. Returns the per-layer kvssm_forward results ("out" is
+    [T, H, hd], before the bf16 rounding that feeds the next layer)."""
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    widths = [("q", d), ("dt_k", d), ("dt_v", d), ("bm_k", N), ("cm_k", N), ("bm_v", N), ("cm_v", N)]
+    results = []
+    for l, lay in enumerate(layers):
+        proj = round_to_bf16(linear(x, lay["w"]))
+        inp = {"x": x}
+        start = 0
+        for name, wd in widths:
+            inp[name] = proj[:, start:start + wd]
+            start += wd
+        for k, v in lay["params"].items():
+            inp[k] = np.asarray(v, np.float64)
+        res = kvssm_forward(inp, seq_cu, H, hd, P, first_layer + l, L, mode)
+        results.append(res)
+        x = round_to_bf16(res["out"].reshape(T, d))
+    return results
+
+
+# ----------------------------------------------------------------------------------------
 # Decode with a cache of boundary states plus the L most recent tokens (pith.science
 # "Core claim": at inference only the boundary states are cached; "If this is right":
 # KV-cache shrinks by about P; leading tokens stay uncompressed).

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "attamba_oracle.py")
 PINS = ["test_oracle_segment.py", "test_oracle_scan.py", "test_oracle_attention.py",
         "test_oracle_decode.py", "test_oracle_proj.py", "test_oracle_backward.py",
-        "test_oracle_block.py"]
+        "test_oracle_block.py", "test_oracle_stack.py"]
 
 MUTANTS = [
     ("decay uses the previous step size", "decay = np.exp(delta[k][:, None] * A)",
@@ -65,6 +65,12 @@ MUTANTS = [
     ("convolution bias dropped", "            acc = b.copy()", "            acc = np.zeros(d)"),
     ("SiLU replaced by the logistic function", "return v / (1.0 + np.exp(-v))", "return 1.0 / (1.0 + np.exp(-v))"),
     ("gate applied without SiLU", "return y if z is None else y * silu(z)", "return y if z is None else y * z"),
+    ("bf16 rounding keeps one bit too many", "return np.ldexp(np.round(m * 256.0), e - 8)",
+     "return np.ldexp(np.round(m * 512.0), e - 9)"),
+    ("stack feeds the unrounded output on", "        x = round_to_bf16(res[\"out\"].reshape(T, d))",
+     "        x = res[\"out\"].reshape(T, d)"),
+    ("stack layers all at the first offset", "res = kvssm_forward(inp, seq_cu, H, hd, P, first_layer + l, L, mode)",
+     "res = kvssm_forward(inp, seq_cu, H, hd, P, first_layer, L, mode)"),
     ("block skip term on the raw input", "    y, _ = selective_scan(xc, dt, dt_bias, A, Bm, Cm, D, chunk_cu)\n    return y if z",
      "    y, _ = selective_scan(xc, dt, dt_bias, A, Bm, Cm, D, chunk_cu)\n    y = y + D * (np.asarray(x) - xc)\n    return y if z"),
 ]

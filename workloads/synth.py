@@ -137,6 +137,19 @@ def make_block_inputs(inp: PrefillInputs, K: int, seed: int, gate: bool = True) 
     return out
 
 
+def make_stack(d: int, N: int, n_layers: int, seed: int) -> list:
+    """Weights of a stack of layers: per layer the stacked projection weight [3 d + 4 N, d]
+    (q, dt_K, dt_V, Bm_K, Cm_K, Bm_V, Cm_V rows, each ~ N(0, 0.02^2), bf16) and the SSM
+    parameters drawn as for make_prefill (float32). CPU tensors."""
+    layers = []
+    for l in range(n_layers):
+        rng = np.random.default_rng((seed, 5, l))
+        params = _params(rng, d, N)
+        w = rng.standard_normal((3 * d + 4 * N, d), dtype=np.float32) * np.float32(0.02)
+        layers.append({"w": torch.from_numpy(w).to(torch.bfloat16), "params": params})
+    return layers
+
+
 @dataclass
 class ProjInputs:
     """Layer input x [T, d] and the stacked projection weight w [n_out, d] (one row per
