@@ -650,9 +650,12 @@ PROBE_OPS = {0: "v_fma_f32 VOP3 (VGPR operands)", 1: "v_fma_f32 VOP3 (one SGPR o
              10: "v_fmamk_f32 VOP2 (literal operand)", 11: "v_cvt_pk_bf16_f32 + v_perm_b32 (two VOP3)",
              12: "v_dot2 bf16 pairs, f32 accumulator",
              13: "v_exp_f32 VOP3 + independent v_fmac_f32 VOP2 pair",
-             14: "v_mfma_f32_32x32x16_bf16 + 8 independent v_fmac_f32 VOP2 (per MFMA)"}
+             14: "v_mfma_f32_32x32x16_bf16 + 8 independent v_fmac_f32 VOP2 (per MFMA)",
+             15: "v_mfma_f32_32x32x16_bf16 + 8 independent v_exp_f32 (per MFMA)",
+             16: "v_mfma_f32_32x32x16_bf16 + 8 independent v_fma_f32 VOP3 (per MFMA)"}
 PROBE_ITERS = {0: 20000, 1: 20000, 2: 20000, 3: 8000, 4: 2000, 5: 1000, 6: 20000, 7: 20000,
-               8: 20000, 9: 8000, 10: 20000, 11: 20000, 12: 20000, 13: 8000, 14: 2000}
+               8: 20000, 9: 8000, 10: 20000, 11: 20000, 12: 20000, 13: 8000, 14: 2000, 15: 2000,
+               16: 2000}
 
 
 def probe_per_simd(rec, ops_per_wave, W):
@@ -732,6 +735,8 @@ def bench_valu_issue(args):
         "exp_plus_fmac_pair_clocks_W4": clk(13),
         "mfma_plus_8_fmac_clocks_W1": clk(14, "W1"),
         "mfma_plus_8_fmac_clocks_W2": clk(14, "W2"),
+        "mfma_plus_8_exp_clocks_W2": clk(15, "W2"),
+        "mfma_plus_8_vop3_fma_clocks_W2": clk(16, "W2"),
         "sgpr_operand_fma_slots_W4": ratio(clk(1), fma),
         "exp_vop3_slots_W4": ratio(clk(3), fma),
         "scan_update_clocks_W4": clk(5),

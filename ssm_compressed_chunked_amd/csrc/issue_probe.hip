@@ -34,7 +34,9 @@ enum Op {
   kCvtPk = 11,    // v_cvt_pk_bf16_f32 (two float32 to a bf16 pair)
   kDot2 = 12,     // v_dot2 of a bf16 pair with a bf16 pair, float32 accumulator
   kExpFmac = 13,  // v_exp_f32 chains interleaved with independent v_fmac_f32 chains
-  kMfmaFmac = 14  // v_mfma_f32_32x32x16_bf16 chains with 8 independent v_fmac_f32 per MFMA
+  kMfmaFmac = 14, // v_mfma_f32_32x32x16_bf16 chains with 8 independent v_fmac_f32 per MFMA
+  kMfmaExp = 15,  // the same with 8 independent v_exp_f32 per MFMA
+  kMfmaFma3 = 16  // the same with 8 independent v_fma_f32 (VOP3) per MFMA
 };
 
 constexpr int kChains = 8;      // independent chains per lane (VALU ops)
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int iters, float s, co
     for (int j = 0; j < kMfmaChains; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) result += m[j][v];
-  } else if constexpr (OP == kMfmaFmac) {
+  } else if constexpr (OP == kMfmaFmac || OP == kMfmaExp || OP == kMfmaFma3) {
     bf16x8 fa, fb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -119,7 +121,12 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int iters, float s, co
         for (int j = 0; j < kMfmaChains; ++j) {
           m[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, m[j], 0, 0, 0);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc[(j * 8 + k) % kStates] = fmaf(a, b, acc[(j * 8 + k) % kStates]);
+          for (int k = 0; k < 8; ++k) {
+            float& r = acc[(j * 8 + k) % kStates];
+            if constexpr (OP == kMfmaFmac) r = fmaf(a, b, r);
+            else if constexpr (OP == kMfmaExp) r = __builtin_amdgcn_exp2f(-r);
+            else r = fmaf(r, a, b);
+          }
         }
     }
     stamp(c1, r1);
@@ -219,7 +226,8 @@ int attamba_probe_ops_per_iter(int op) {
     case kFmamk: case kCvtPk: case kDot2: return kChains * kUnroll;
     case kExpMul: return kChains * kUnroll;            // exp + mul pairs
     case kExpFmac: return kChains * kUnroll / 2;       // exp + fmac pairs
-    case kMfma: case kMfmaFmac: return kMfmaChains * kUnroll / 2;   // MFMAs (with 8 fmac each)
+    case kMfma: case kMfmaFmac: case kMfmaExp: case kMfmaFma3:
+      return kMfmaChains * kUnroll / 2;   // MFMAs (each with 8 VALU instructions beside it)
     case kScanUpdate: return kStates * kTokens;   // state updates per iteration
     default: return -1;
   }
@@ -254,6 +262,8 @@ int attamba_probe_issue(int op, int blocks, int iters, float s, const float* vin
     case kDot2: hipLaunchKernelGGL(issue_probe_kernel<kDot2>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
     case kExpFmac: hipLaunchKernelGGL(issue_probe_kernel<kExpFmac>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
     case kMfmaFmac: hipLaunchKernelGGL(issue_probe_kernel<kMfmaFmac>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
+    case kMfmaExp: hipLaunchKernelGGL(issue_probe_kernel<kMfmaExp>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
+    case kMfmaFma3: hipLaunchKernelGGL(issue_probe_kernel<kMfmaFma3>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
     default: return 1;
   }
   return static_cast<int>(hipGetLastError());
