@@ -38,11 +38,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # VALU issue capacity: 256 CUs x 4 SIMDs x 32 fp32 lanes per clock x 2.4 GHz = 78.6 T
 # lane-instruction slots per second (the 157.3 TFLOP/s fp32 vector peak counts an FMA as two).
 VALU_SLOTS_PER_S = 256 * 4 * 32 * 2.4e9
-# VALU issue slots per state update of the scan: multiply for the exponent, v_exp_f32, multiply
-# for the input term, FMA state, FMA output. A wave64 v_exp_f32 occupies the SIMD 2.75 times as
-# long as a wave64 FMA (5.5 vs 2.0 clocks at 4 waves per SIMD; `--workload valu_issue` measures
-# both, and the whole update, on the part), so it counts 2.75.
-SLOTS_PER_UPDATE = 6.75
+# Issue costs measured by `--workload valu_issue` (shader clocks per wave64 instruction per SIMD
+# with several waves per SIMD): a VOP2 instruction with VGPR operands (v_mul, v_fmac) 2.2, and
+# v_exp_f32 8.1. One slot is one such VOP2 instruction, so v_exp_f32 counts 8.1 / 2.2 = 3.7.
+EXP_SLOTS = 3.7
+# Slots per state update of the scan in its cheapest form: multiply for the exponent, v_exp_f32,
+# multiply for the input term, FMA state, FMA output (the kernel issues the last two with an SGPR
+# row operand, ~4.1 clocks each; that penalty is the kernel's, not the algorithm's).
+SLOTS_PER_UPDATE = 4.0 + EXP_SLOTS
 PROBE_LIB = os.path.join(ROOT, "ssm_compressed_chunked_amd", "libattamba_probe.so")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -531,10 +534,10 @@ def cpu_baseline_train(cfg, inp, dout, T_full, scan_budget_s=3.0, attn_budget_s=
 
 
 # minimal VALU slots per state update of the scan backward: the forward recompute (decay
-# multiply, v_exp_f32 at 2.75 slots, input multiply, state FMA), g h for dCm, and the reverse
-# step (dh FMA, dBm multiply, du FMA, decay recomputed, dh e, w = dh e h_prev, dA and ddelta
-# FMAs), plus one add each for the channel sums of dCm and dBm
-SLOTS_PER_UPDATE_BWD = 5.75 + 1.0 + 10.75 + 2.0
+# multiply, v_exp_f32, input multiply, state FMA), g h for dCm, and the reverse step (dh FMA,
+# dBm multiply, du FMA, decay recomputed (multiply and v_exp_f32), dh e, w = dh e h_prev, dA and
+# ddelta FMAs), plus one add each for the channel sums of dCm and dBm
+SLOTS_PER_UPDATE_BWD = (3.0 + EXP_SLOTS) + 1.0 + (8.0 + EXP_SLOTS) + 2.0
 
 
 def bench_train(args):

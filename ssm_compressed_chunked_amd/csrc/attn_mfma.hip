@@ -77,16 +77,19 @@ __global__ __launch_bounds__(NT) void attn_mfma_kernel(AttnParams p) {
   constexpr int BM = 128;         // query rows per workgroup (4 waves x 32)
   __shared__ Smem<HD> sm;
 
-  // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. All query tiles
-  // of one (sequence, head) are placed on one XCD, consecutively, so that its boundary-state
-  // prefix is fetched into that L2 once; within a (sequence, head) the tiles with the most
-  // keys (the last rows) are issued first so that light tiles form the tail of the grid.
+  // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. Consecutive ids
+  // take the same query tile of consecutive (sequence, head) pairs, and the (sequence, head)
+  // count is padded to a multiple of 8, so every query tile of one (sequence, head) lands on
+  // the same XCD, whose L2 then holds that pair's boundary-state prefix (256 KB per pair at
+  // hd 64 and 8 192 tokens, 8 pairs per XCD at a time). The last query tiles, which see the most
+  // keys, are issued first over the whole grid, so the tail of the grid is made of light tiles.
   const int n_qt = ceil_div(p.max_seqlen, BM);
-  const int id = blockIdx.x, slot = id >> 3;
-  const int bh = (slot / n_qt) * 8 + (id & 7);
+  const int n_bh8 = ceil_div(p.S * p.H, 8) * 8;
+  const int id = blockIdx.x;
+  const int bh = id % n_bh8;
   if (bh >= p.S * p.H) return;
   const int s = bh / p.H, h = bh % p.H;
-  const int qt = n_qt - 1 - slot % n_qt;
+  const int qt = n_qt - 1 - id / n_bh8;
   const int s0 = p.seq_cu[s], s1 = p.seq_cu[s + 1];
   const int r0 = s0 + qt * BM;
   if (r0 >= s1) return;
