@@ -78,18 +78,20 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkv_mfma_kernel(AttnBwdParams bp)
   __shared__ DkvSmem<HD> sm;
   const AttnParams& p = bp.f;
 
-  // Workgroups go round-robin to the 8 XCDs; all key tiles of one (sequence, head) sit on one
-  // XCD, boundary tiles (seen by the most rows) first. A boundary tile is seen by every later
-  // row of its sequence, so its query rows are split over ns workgroups (parts), each walking a
-  // contiguous share of the query tiles; their float32 partial sums are added by a finalize
-  // launch. Per-token key tiles are seen by a few hundred rows and are not split.
+  // Workgroups go round-robin to the 8 XCDs. Consecutive ids take the same key tile of
+  // consecutive (sequence, head) pairs (the pair count padded to a multiple of 8), so all key
+  // tiles of one pair sit on one XCD, and the boundary tiles (seen by the most rows) go first
+  // over the whole grid. A boundary tile is seen by every later row of its sequence, so its
+  // query rows are split over ns workgroups (parts), each walking a contiguous share of the query
+  // tiles; their float32 partial sums are added by a finalize launch. Per-token key tiles are
+  // seen by a few hundred rows and are not split.
   const int ns = bp.dkv_split;
-  const int n_kt = (ns + 1) * ceil_div(p.max_seqlen, BK);
-  const int id = blockIdx.x, slot = id >> 3;
-  const int bh = (slot / n_kt) * 8 + (id & 7);
+  const int n_bh8 = ceil_div(p.S * p.H, 8) * 8;
+  const int id = blockIdx.x;
+  const int bh = id % n_bh8;
   if (bh >= p.S * p.H) return;
   const int s = bh / p.H, h = bh % p.H;
-  const int ks = slot % n_kt;
+  const int ks = id / n_bh8;
   const int s0 = p.seq_cu[s], s1 = p.seq_cu[s + 1];
   if (s1 <= s0) return;
   const int c0 = p.token_chunk[s0];
@@ -336,12 +338,15 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_mfma_kernel(AttnBwdParams bp) 
   __shared__ DqSmem<HD> sm;
   const AttnParams& p = bp.f;
 
+  // grid order as in the forward: the same query tile of consecutive (sequence, head) pairs,
+  // the last query tiles (the most keys) first over the whole grid
   const int n_qt = ceil_div(p.max_seqlen, BQ);
-  const int id = blockIdx.x, slot = id >> 3;
-  const int bh = (slot / n_qt) * 8 + (id & 7);
+  const int n_bh8 = ceil_div(p.S * p.H, 8) * 8;
+  const int id = blockIdx.x;
+  const int bh = id % n_bh8;
   if (bh >= p.S * p.H) return;
   const int s = bh / p.H, h = bh % p.H;
-  const int qt = n_qt - 1 - slot % n_qt;
+  const int qt = n_qt - 1 - id / n_bh8;
   const int s0 = p.seq_cu[s], s1 = p.seq_cu[s + 1];
   const int r0 = s0 + qt * BQ;
   if (r0 >= s1) return;

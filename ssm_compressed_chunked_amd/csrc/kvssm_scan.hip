@@ -24,9 +24,8 @@
 // loads up front and the same one-token row prefetch.
 // The Mamba-block variant (BLK) adds, per lane, a causal depthwise convolution of up to 4 taps
 // with SiLU on the scan's input and a SiLU gate on its output. The convolution restarts at every
-// chunk start like the state, so it needs no tokens from before the chunk: inside a block it
-// reads the block's own x registers, and across the blocks of a long chunk it carries the last
-// three inputs.
+// chunk start like the state, so it needs no tokens from before the chunk: each lane keeps the
+// last three inputs of its channel as a window that restarts at zero with every chunk.
 #include "common.h"
 #include "kernels.h"
 
@@ -79,16 +78,16 @@ struct ConvLane {
       if (k < K) w4[4 - K + k] = w[c * K + k];
     b = bias[c];
   }
-  // silu of the convolution at block token j, from the block's inputs xs and the three inputs
-  // before the block (prev[0] is the oldest; zero before the chunk start)
-  template <int PU>
-  __device__ __forceinline__ float at(const float (&xs)[PU], const float (&prev)[3], int j) const {
-    float acc = b;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = j - 3 + k;
-      acc = fmaf(w4[k], s >= 0 ? xs[s] : prev[3 + s], acc);
-    }
+  // silu of the convolution at the current token xr, whose three predecessors in the chunk are
+  // win[0..2] (win[0] the oldest; zero before the chunk start); then xr joins the window
+  __device__ __forceinline__ float next(float (&win)[3], float xr) const {
+    float acc = fmaf(w4[0], win[0], b);
+    acc = fmaf(w4[1], win[1], acc);
+    acc = fmaf(w4[2], win[2], acc);
+    acc = fmaf(w4[3], xr, acc);
+    win[0] = win[1];
+    win[1] = win[2];
+    win[2] = xr;
     return silu_f32(acc);
   }
 };
@@ -185,8 +184,10 @@ __device__ __forceinline__ void rows_ready(uint32_t b0, uint32_t c0) {
 
 template <typename T, int N, int PU, int CPW, bool BLK>
 // bf16 with N = 16 (the common case) is held to 7 waves per SIMD (72 VGPRs; the other-length
-// path would otherwise take 73 and lose a wave); the other instances are left unconstrained.
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 && sizeof(T) == 2 && !BLK ? 7 : 1))) void kvssm_scan_kernel(
+// path would otherwise take 73 and lose a wave), and its Mamba-block instance to 5 (96 VGPRs and
+// a 52-byte spill instead of 124 VGPRs at 4 waves: 315 us against 340 us at the prefill shape);
+// the other instances are left unconstrained.
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 && sizeof(T) == 2 ? (BLK ? 5 : 7) : 1))) void kvssm_scan_kernel(
     ScanShape sh, const int32_t* __restrict__ chunk_cu, const int32_t* __restrict__ seq_cu,
     SideArgs<T> ka, SideArgs<T> va) {
   int side, group, ctile;
@@ -240,14 +241,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
         dts[j] = to_f32(dt[o]);
         if (gated) zs[j] = to_f32(a.z[o]);
       }
-      if (conv) {   // the chunk starts here: nothing before it counts
-        const float prev[3] = {0.f, 0.f, 0.f};
-        float xc[PU];
-#pragma unroll
-        for (int j = 0; j < PU; ++j) xc[j] = cv.at<PU>(xs, prev, j);
-#pragma unroll
-        for (int j = 0; j < PU; ++j) xs[j] = xc[j];
-      }
+      float win[3] = {0.f, 0.f, 0.f};   // the chunk starts here: nothing before it counts
       typename SsmLane<T, N>::Rows rn, rc;
       SsmLane<T, N>::load_rows(bm + cs * N, cm + cs * N, rn);
 #pragma unroll
@@ -257,15 +251,16 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
         rows_ready(rc.b[0], rc.c[0]);
         if (j + 1 < PU) SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rn);
         order_point();
-        if (j == 0) out = s.template step<true>(xs[j], dts[j], rc);
-        else out = s.template step<false>(xs[j], dts[j], rc);
+        const float xin = conv ? cv.next(win, xs[j]) : xs[j];
+        if (j == 0) out = s.template step<true>(xin, dts[j], rc);
+        else out = s.template step<false>(xin, dts[j], rc);
         if (gated) out *= silu_f32(zs[j]);
         y[t * d + c] = from_f32<T>(out);
       }
     } else {
       // any other length: blocks of up to PU tokens, each with its x/dt loads issued up front
       // (the state runs on across the blocks of a chunk)
-      float prev[3] = {0.f, 0.f, 0.f};   // convolution inputs before the block (chunk start: 0)
+      float win[3] = {0.f, 0.f, 0.f};   // the last three inputs (chunk start: 0)
       for (int bs = cs; bs < ce; bs += PU) {
         const int nb = min(PU, ce - bs);
         float xs[PU], dts[PU], zs[PU];
@@ -275,26 +270,6 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
           xs[j] = to_f32(x[o]);
           dts[j] = to_f32(dt[o]);
           if (gated) zs[j] = to_f32(a.z[o]);
-        }
-        if (conv) {
-          float xc[PU];
-#pragma unroll
-          for (int j = 0; j < PU; ++j) xc[j] = cv.at<PU>(xs, prev, j);
-          // the last three raw inputs up to the block's end (nb is uniform over the wave)
-          float w[PU + 3];
-#pragma unroll
-          for (int i = 0; i < 3; ++i) w[i] = prev[i];
-#pragma unroll
-          for (int j = 0; j < PU; ++j) w[3 + j] = xs[j];
-#pragma unroll
-          for (int m = 1; m <= PU; ++m)
-            if (nb == m) {
-              prev[0] = w[m];
-              prev[1] = w[m + 1];
-              prev[2] = w[m + 2];
-            }
-#pragma unroll
-          for (int j = 0; j < PU; ++j) xs[j] = xc[j];
         }
         typename SsmLane<T, N>::Rows rn, rc;
         SsmLane<T, N>::load_rows(bm + bs * N, cm + bs * N, rn);
@@ -306,8 +281,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
             rows_ready(rc.b[0], rc.c[0]);
             if (j + 1 < nb) SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rn);
             order_point();
-            if (j == 0 && bs == cs) out = s.template step<true>(xs[j], dts[j], rc);
-            else out = s.template step<false>(xs[j], dts[j], rc);
+            const float xin = conv ? cv.next(win, xs[j]) : xs[j];
+            if (j == 0 && bs == cs) out = s.template step<true>(xin, dts[j], rc);
+            else out = s.template step<false>(xin, dts[j], rc);
             if (gated) out *= silu_f32(zs[j]);
             y[t * d + c] = from_f32<T>(out);
           }
