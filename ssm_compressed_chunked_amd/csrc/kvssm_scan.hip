@@ -182,22 +182,62 @@ __device__ __forceinline__ void rows_ready(uint32_t b0, uint32_t c0) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Per-lane access to channel c of a token-major [T, d] tensor. With BUF (bf16 only) the tensor
+// goes through a buffer resource: the lane's byte offset 2c is fixed and the token's offset 2td
+// is a scalar, so no per-token vector address arithmetic is issued (T d < 2^31, so both offsets
+// and the size fit in 32 bits; 174 against 177 us at the prefill shape). Otherwise plain
+// pointers (the Mamba-block instance measured 375 against 305-322 us with buffer accesses).
+template <typename T, bool BUF>
+struct Column {
+  const T* p;
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ void init(const T* q, int T_rows, int d) {
+    p = q;
+    if constexpr (BUF)
+      r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(q), (short)0,
+                                            static_cast<int>(2u * static_cast<uint32_t>(T_rows) *
+                                                             static_cast<uint32_t>(d)),
+                                            0x00020000);
+  }
+  // element (t, c): row offset rd = t d (wave-uniform), channel c
+  __device__ __forceinline__ float load(int rd, int c) const {
+    if constexpr (BUF) {
+      const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(r, 2u * c, 2u * rd, 0);
+      return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    } else {
+      return to_f32(p[rd + c]);
+    }
+  }
+  __device__ __forceinline__ void store(float v, int rd, int c) const {
+    if constexpr (BUF) {
+      const __bf16 b = from_f32<__bf16>(v);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, b), r, 2u * c,
+                                            2u * rd, 0);
+    } else {
+      const_cast<T*>(p)[rd + c] = from_f32<T>(v);
+    }
+  }
+};
+
 template <typename T, int N, int PU, int CPW, bool BLK>
-// bf16 with N = 16 (the common case) is held to 7 waves per SIMD (72 VGPRs; the other-length
-// path would otherwise take 73 and lose a wave), and its Mamba-block instance to 5 (96 VGPRs and
-// a 52-byte spill instead of 124 VGPRs at 4 waves: 315 us against 340 us at the prefill shape);
-// the other instances are left unconstrained.
+// bf16 with N = 16 (the common case) is held to 7 waves per SIMD (65 VGPRs; 8 waves at 64 VGPRs
+// measured the same), and its Mamba-block instance to 5 (96 VGPRs and a 52-byte spill instead of
+// 124 VGPRs at 4 waves: 315 us against 340 us at the prefill shape); the other instances are
+// left unconstrained.
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 && sizeof(T) == 2 ? (BLK ? 5 : 7) : 1))) void kvssm_scan_kernel(
     ScanShape sh, const int32_t* __restrict__ chunk_cu, const int32_t* __restrict__ seq_cu,
     SideArgs<T> ka, SideArgs<T> va) {
   int side, group, ctile;
   if (!map_block(sh, side, group, ctile)) return;
   const SideArgs<T> a = side ? va : ka;
-  const T* __restrict__ x = a.x;
-  const T* __restrict__ dt = a.dt;
   const T* __restrict__ bm = a.bm;
   const T* __restrict__ cm = a.cm;
-  T* __restrict__ y = a.y;
+  constexpr bool kBuf = sizeof(T) == 2 && !BLK;
+  Column<T, kBuf> x, dt, y, z;
+  x.init(a.x, sh.T, sh.d);
+  dt.init(a.dt, sh.T, sh.d);
+  y.init(a.y, sh.T, sh.d);
+  if (BLK && a.z) z.init(a.z, sh.T, sh.d);
   const int lane = threadIdx.x;
   const int c = ctile * kWave + lane;
   const int d = sh.d;
@@ -236,10 +276,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
       float xs[PU], dts[PU], zs[PU];
 #pragma unroll
       for (int j = 0; j < PU; ++j) {
-        const int o = (cs + j) * d + c;
-        xs[j] = to_f32(x[o]);
-        dts[j] = to_f32(dt[o]);
-        if (gated) zs[j] = to_f32(a.z[o]);
+        const int rd = (cs + j) * d;
+        xs[j] = x.load(rd, c);
+        dts[j] = dt.load(rd, c);
+        if (gated) zs[j] = z.load(rd, c);
       }
       float win[3] = {0.f, 0.f, 0.f};   // the chunk starts here: nothing before it counts
       typename SsmLane<T, N>::Rows rn, rc;
@@ -255,7 +295,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
         if (j == 0) out = s.template step<true>(xin, dts[j], rc);
         else out = s.template step<false>(xin, dts[j], rc);
         if (gated) out *= silu_f32(zs[j]);
-        y[t * d + c] = from_f32<T>(out);
+        y.store(out, t * d, c);
       }
     } else {
       // any other length: blocks of up to PU tokens, each with its x/dt loads issued up front
@@ -266,10 +306,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
         float xs[PU], dts[PU], zs[PU];
 #pragma unroll
         for (int j = 0; j < PU; ++j) {   // past the block's end: its last token again (unused)
-          const int o = (bs + min(j, nb - 1)) * d + c;
-          xs[j] = to_f32(x[o]);
-          dts[j] = to_f32(dt[o]);
-          if (gated) zs[j] = to_f32(a.z[o]);
+          const int rd = (bs + min(j, nb - 1)) * d;
+          xs[j] = x.load(rd, c);
+          dts[j] = dt.load(rd, c);
+          if (gated) zs[j] = z.load(rd, c);
         }
         typename SsmLane<T, N>::Rows rn, rc;
         SsmLane<T, N>::load_rows(bm + bs * N, cm + bs * N, rn);
@@ -285,7 +325,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
             if (j == 0 && bs == cs) out = s.template step<true>(xin, dts[j], rc);
             else out = s.template step<false>(xin, dts[j], rc);
             if (gated) out *= silu_f32(zs[j]);
-            y[t * d + c] = from_f32<T>(out);
+            y.store(out, t * d, c);
           }
         }
       }
