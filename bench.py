@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="decode workloads: number of sequences (default: the workload's)")
     return ap.parse_args()
 
 
@@ -325,6 +327,8 @@ def bench_decode(args):
     from workloads import DECODE_CONFIGS, make_decode
 
     cfg = DECODE_CONFIGS[args.workload]
+    if args.batch is not None:
+        cfg = cfg.with_(B=args.batch)
     n_bound = att.count_chunks([0, cfg.ctx], cfg.P, cfg.layer_idx)
     o = cfg.layer_idx % cfg.P
     if (cfg.ctx - o) % cfg.P != 0:
@@ -364,7 +368,8 @@ def bench_decode(args):
     kv_bytes = keys * cfg.B * cfg.H * cfg.hd * 2 * e
     state_bytes = cfg.steps * 2 * 2 * cfg.B * cfg.d * cfg.N * 4
     gbps = (kv_bytes + state_bytes) / wall / 1e9
-    traffic = measured_traffic("decode_step", ["decode.hip", "common.h"], args.workload)
+    traffic = (measured_traffic("decode_step", ["decode.hip", "common.h"], args.workload)
+               if args.batch is None else None)
     line = {"metric": "decode tokens/s (boundary-state cache)", "value": round(cfg.B * cfg.steps / wall, 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": cfg.steps, "warmup": args.warmup,
             "ms_per_step": round(wall * 1e3 / cfg.steps, 4), "higher_is_better": True,

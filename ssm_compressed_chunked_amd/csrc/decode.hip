@@ -24,9 +24,12 @@ namespace {
 constexpr int kSplit = 256;          // keys per split workgroup (the finest split)
 constexpr int kSplitWide = 1024;     // bf16 caches whose grid keeps kWideMinGroups workgroups
 // The 1024-key kernel takes 234 VGPRs (2 waves per SIMD), so a CU holds two of its 4-wave
-// workgroups and the chip 512; 4096 workgroups keep the grid at least 8 such rounds deep, so
-// the longer splits do not leave a ragged last round. Below that the 256-key split is used.
-constexpr int kWideMinGroups = 8 * 2 * 256;
+// workgroups and the chip 512. With at least 4 such rounds (2048 workgroups) the longer splits
+// win; with fewer the grid runs short of workgroups and the 256-key split is used. Measured at
+// 32 heads of 128 and 32 768 tokens of context: 1024-key splits 45 600 / 47 466 / 48 004 tokens/s
+// against 45 300 / 45 434 / 45 448 at 8 / 12 / 16 sequences (2 304 / 3 456 / 4 608 workgroups),
+// 256-key splits 44 687 / 32 008 against 43 294 / 26 205 at 6 / 1 sequences.
+constexpr int kWideMinGroups = 4 * 2 * 256;
 constexpr int kSplitThreads = 256;
 constexpr int kUpdLanes = 4;         // lanes per (sequence, channel) in the state update
 
