@@ -10,11 +10,13 @@
 //
 // The product is computed transposed, C^T = W x^T, so that an accumulator lane holds one token
 // and four consecutive features per register group: each lane stores 8 contiguous bytes.
-// Workgroup = 4 waves, tile 128 features x 128 tokens, K steps of 64; wave (wf, wt) owns the
-// 64 x 64 quarter (wf, wt) as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16. Both operands are
-// K-contiguous, so every operand is one ds_read_b128 from an LDS tile whose 16-byte segments are
-// XOR-swizzled by row (conflict-free for 8 consecutive rows). Tiles come from HBM straight into
-// LDS (global_load_lds_dwordx4) into two buffers, one barrier per K step.
+// Workgroup = 8 waves (2 per SIMD), tile 256 features x 256 tokens, K steps of 64; wave
+// (wf, wt) owns 64 features x 128 tokens as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16. Both
+// operands are K-contiguous, so every operand is one ds_read_b128 from an LDS tile whose 16-byte
+// segments are XOR-swizzled by row (conflict-free for 8 consecutive rows). Tiles come from HBM
+// straight into LDS (global_load_lds_dwordx4) into two buffers (128 KB, one workgroup per CU),
+// one barrier per K step. The large tile halves the bytes each CU pulls from L2 per FLOP
+// against 128 x 128 tiles, whose data-return path was busy 83 % of the time.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,12 +28,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int TM = 128;     // features per tile
-constexpr int TN = 128;     // tokens per tile
+constexpr int TM = 256;     // features per tile
+constexpr int TN = 256;     // tokens per tile
 constexpr int TK = 64;      // K per step
-constexpr int NT = 256;     // threads per workgroup
-constexpr int kChunks = TM * TK * 2 / 1024;     // 1 KB chunks per operand tile (16)
-constexpr int kChunksPerWave = kChunks / 4;     // 4
+constexpr int NW = 8;       // waves per workgroup
+constexpr int NT = NW * 64; // threads per workgroup
+constexpr int kChunks = TM * TK * 2 / 1024;     // 1 KB chunks per operand tile (32)
+constexpr int kChunksPerWave = kChunks / NW;    // 4
 
 // element offset of logical 16-byte segment s of tile row r (8 segments per row)
 __device__ __forceinline__ int seg_off(int r, int s) { return r * TK + 8 * (s ^ (r & 7)); }
@@ -43,21 +46,21 @@ struct ProjTile {
 
 __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
   __shared__ ProjTile sm;
-  // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. XCD x takes the
-  // feature tiles x, x + 8, x + 16, ... (their weight rows, about n_out / 8 x d, stay in its
-  // L2) for every token tile in turn; the token tiles' x rows are shared through L2 by the
-  // XCD's workgroups running at the same time.
-  const int n_ft = ceil_div(p.n_out, TM);
+  // Workgroups go round-robin to the 8 XCDs (id mod 8), each with its own L2. XCD x owns the
+  // token tiles x, x + 8, x + 16, ... and walks, for each feature tile in turn, all of them; the
+  // workgroups running at once on an XCD then share a few weight tiles and the XCD's token rows
+  // through its L2.
+  const int n_ft = ceil_div(p.n_out, TM), n_tt = ceil_div(p.T, TN);
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int n_fx = (n_ft - xcd + 7) / 8;          // feature tiles of this XCD
-  const int n_fmax = (n_ft + 7) / 8;
-  if (slot % n_fmax >= n_fx) return;
-  const int ft = xcd + 8 * (slot % n_fmax), tt = slot / n_fmax;
-  if (tt * TN >= p.T) return;
+  const int n_tx = (n_tt - xcd + 7) / 8;          // token tiles of this XCD
+  const int n_tmax = (n_tt + 7) / 8;
+  const int m = slot % n_tmax, ft = slot / n_tmax;
+  if (m >= n_tx || ft >= n_ft) return;
+  const int tt = xcd + 8 * m;
   const int f0 = ft * TM, t0 = tt * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wf = wid & 1, wt = wid >> 1;
+  const int wf = wid & 3, wt = wid >> 2;          // 64 features x 128 tokens per wave
   const int d = p.d;
   const __bf16* W = static_cast<const __bf16*>(p.w);
   const __bf16* X = static_cast<const __bf16*>(p.x);
@@ -86,20 +89,20 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
   // operand offsets: block i of this wave's features / block j of its tokens, row l % 32,
   // k segment 2 ks + l / 32
   const int q = lane & 31, hf = lane >> 5;
-  int aoff[2][4], boff[2][4];
+  int aoff[2][4], boff[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      aoff[i][ks] = seg_off(wf * 64 + 32 * i + q, 2 * ks + hf);
-      boff[i][ks] = seg_off(wt * 64 + 32 * i + q, 2 * ks + hf);
-    }
+    for (int i = 0; i < 2; ++i) aoff[i][ks] = seg_off(wf * 64 + 32 * i + q, 2 * ks + hf);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) boff[j][ks] = seg_off(wt * 128 + 32 * j + q, 2 * ks + hf);
+  }
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -114,27 +117,26 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
     const __bf16* sx = sm.x[buf];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 a[2], b[2];
+      bf16x8 a[2], b[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8*>(sw + aoff[i][ks]);
-        b[i] = *reinterpret_cast<const bf16x8*>(sx + boff[i][ks]);
-      }
+      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(sw + aoff[i][ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(sx + boff[j][ks]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of step kt + 1 have landed ...
     __syncthreads();                 // ... and every wave is done with step kt
   }
 
-  // epilogue: block (i, j), register group g: token t0 + 64 wt + 32 j + q, features
+  // epilogue: block (i, j), register group g: token t0 + 128 wt + 32 j + q, features
   // f0 + 64 wf + 32 i + 8 g + 4 hf .. +3 (all four in one output segment)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = t0 + wt * 64 + 32 * j + q;
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + wt * 128 + 32 * j + q;
     if (t >= p.T) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
 
 hipError_t launch_proj_gemm(const ProjParams& p, hipStream_t stream) {
   if (p.T == 0 || p.n_out == 0) return hipSuccess;
-  const int grid = 8 * ceil_div(ceil_div(p.n_out, TM), 8) * ceil_div(p.T, TN);
+  const int grid = 8 * ceil_div(p.n_out, TM) * ceil_div(ceil_div(p.T, TN), 8);
   hipLaunchKernelGGL(proj_gemm_kernel, dim3(grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
