@@ -43,4 +43,41 @@ __device__ __forceinline__ float silu_f32(float v) {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Per-lane access to channel c of a token-major [T, d] tensor. With BUF (bf16 only) the tensor
+// goes through a buffer resource: the lane's byte offset 2c is fixed and the token's offset 2td
+// is a scalar, so no per-token vector address arithmetic is issued (T d < 2^31, so both offsets
+// and the size fit in 32 bits). Otherwise plain pointers.
+template <typename T, bool BUF>
+struct Column {
+  const T* p;
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ void init(const T* q, int T_rows, int d) {
+    p = q;
+    if constexpr (BUF)
+      r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(q), (short)0,
+                                            static_cast<int>(2u * static_cast<uint32_t>(T_rows) *
+                                                             static_cast<uint32_t>(d)),
+                                            0x00020000);
+  }
+  // element (t, c): row offset rd = t d (wave-uniform), channel c
+  __device__ __forceinline__ float load(int rd, int c) const {
+    if constexpr (BUF) {
+      const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(r, 2u * c, 2u * rd, 0);
+      return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    } else {
+      return to_f32(p[rd + c]);
+    }
+  }
+  __device__ __forceinline__ void store(float v, int rd, int c) const {
+    if constexpr (BUF) {
+      const __bf16 b = from_f32<__bf16>(v);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, b), r, 2u * c,
+                                            2u * rd, 0);
+    } else {
+      const_cast<T*>(p)[rd + c] = from_f32<T>(v);
+    }
+  }
+};
+
+
 }  // namespace attamba

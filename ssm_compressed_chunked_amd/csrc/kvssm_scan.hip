@@ -182,43 +182,6 @@ __device__ __forceinline__ void rows_ready(uint32_t b0, uint32_t c0) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Per-lane access to channel c of a token-major [T, d] tensor. With BUF (bf16 only) the tensor
-// goes through a buffer resource: the lane's byte offset 2c is fixed and the token's offset 2td
-// is a scalar, so no per-token vector address arithmetic is issued (T d < 2^31, so both offsets
-// and the size fit in 32 bits; 174 against 177 us at the prefill shape). Otherwise plain
-// pointers (the Mamba-block instance measured 375 against 305-322 us with buffer accesses).
-template <typename T, bool BUF>
-struct Column {
-  const T* p;
-  __amdgpu_buffer_rsrc_t r;
-  __device__ __forceinline__ void init(const T* q, int T_rows, int d) {
-    p = q;
-    if constexpr (BUF)
-      r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(q), (short)0,
-                                            static_cast<int>(2u * static_cast<uint32_t>(T_rows) *
-                                                             static_cast<uint32_t>(d)),
-                                            0x00020000);
-  }
-  // element (t, c): row offset rd = t d (wave-uniform), channel c
-  __device__ __forceinline__ float load(int rd, int c) const {
-    if constexpr (BUF) {
-      const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(r, 2u * c, 2u * rd, 0);
-      return __uint_as_float(static_cast<uint32_t>(v) << 16);
-    } else {
-      return to_f32(p[rd + c]);
-    }
-  }
-  __device__ __forceinline__ void store(float v, int rd, int c) const {
-    if constexpr (BUF) {
-      const __bf16 b = from_f32<__bf16>(v);
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, b), r, 2u * c,
-                                            2u * rd, 0);
-    } else {
-      const_cast<T*>(p)[rd + c] = from_f32<T>(v);
-    }
-  }
-};
-
 template <typename T, int N, int PU, int CPW, bool BLK>
 // bf16 with N = 16 (the common case) is held to 7 waves per SIMD (65 VGPRs; 8 waves at 64 VGPRs
 // measured the same), and its Mamba-block instance to 5 (96 VGPRs and a 52-byte spill instead of
@@ -232,6 +195,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
   const SideArgs<T> a = side ? va : ka;
   const T* __restrict__ bm = a.bm;
   const T* __restrict__ cm = a.cm;
+  // bf16 x, dt, y through buffer resources (174 against 177 us at the prefill shape); the
+  // Mamba-block instance keeps plain pointers (375 against 305-322 us with buffer accesses)
   constexpr bool kBuf = sizeof(T) == 2 && !BLK;
   Column<T, kBuf> x, dt, y, z;
   x.init(a.x, sh.T, sh.d);
