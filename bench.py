@@ -660,10 +660,13 @@ PROBE_OPS = {0: "v_fma_f32 VOP3 (VGPR operands)", 1: "v_fma_f32 VOP3 (one SGPR o
              13: "v_exp_f32 VOP3 + independent v_fmac_f32 VOP2 pair",
              14: "v_mfma_f32_32x32x16_bf16 + 8 independent v_fmac_f32 VOP2 (per MFMA)",
              15: "v_mfma_f32_32x32x16_bf16 + 8 independent v_exp_f32 (per MFMA)",
-             16: "v_mfma_f32_32x32x16_bf16 + 8 independent v_fma_f32 VOP3 (per MFMA)"}
+             16: "v_mfma_f32_32x32x16_bf16 + 8 independent v_fma_f32 VOP3 (per MFMA)",
+             17: "v_mul_f32 VOP2 with a DPP row-broadcast operand",
+             18: "v_fmac_f32 VOP2 with a DPP row-broadcast operand",
+             19: "scan state update with DPP row-broadcast row operands (v_mul, v_exp, v_mul_dpp, v_fmac, v_fmac_dpp)"}
 PROBE_ITERS = {0: 20000, 1: 20000, 2: 20000, 3: 8000, 4: 2000, 5: 1000, 6: 20000, 7: 20000,
                8: 20000, 9: 8000, 10: 20000, 11: 20000, 12: 20000, 13: 8000, 14: 2000, 15: 2000,
-               16: 2000}
+               16: 2000, 17: 20000, 18: 20000, 19: 1000}
 
 
 def probe_per_simd(rec, ops_per_wave, W):
@@ -748,6 +751,10 @@ def bench_valu_issue(args):
         "sgpr_operand_fma_slots_W4": ratio(clk(1), fma),
         "exp_vop3_slots_W4": ratio(clk(3), fma),
         "scan_update_clocks_W4": clk(5),
+        "mul_dpp_clocks_W4": clk(17),
+        "fmac_dpp_clocks_W4": clk(18),
+        "scan_update_dpp_clocks_W2": clk(19, "W2"),
+        "scan_update_clocks_W2": clk(5, "W2"),
         "scan_update_slots_W4": ratio(clk(5), fma),
         "mfma_32x32x16_clocks_W4": clk(4),
         "slots_per_update_used_by_prefill_line": SLOTS_PER_UPDATE,

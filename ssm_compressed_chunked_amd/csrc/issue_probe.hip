@@ -36,7 +36,10 @@ enum Op {
   kExpFmac = 13,  // v_exp_f32 chains interleaved with independent v_fmac_f32 chains
   kMfmaFmac = 14, // v_mfma_f32_32x32x16_bf16 chains with 8 independent v_fmac_f32 per MFMA
   kMfmaExp = 15,  // the same with 8 independent v_exp_f32 per MFMA
-  kMfmaFma3 = 16  // the same with 8 independent v_fma_f32 (VOP3) per MFMA
+  kMfmaFma3 = 16, // the same with 8 independent v_fma_f32 (VOP3) per MFMA
+  kMulDpp = 17,   // v_mul_f32 whose first operand is lane n of each row of 16 (DPP row_newbcast)
+  kFmacDpp = 18,  // v_fmac_f32 with such a broadcast operand
+  kScanDpp = 19   // the scan's state update with the rows as broadcast operands of VGPRs
 };
 
 constexpr int kChains = 8;      // independent chains per lane (VALU ops)
@@ -58,6 +61,39 @@ __device__ __forceinline__ void stamp(uint64_t& clk, uint64_t& rt) {
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_sched_barrier(0);
 }
+
+// x * (lane n of each 16-lane row of v), and acc + (lane n of each row of v) * x, with the
+// broadcast as a DPP operand of the VALU instruction (gfx90a and later)
+template <int n>
+__device__ __forceinline__ float mul_bcast(float v, float x) {
+  float r;
+  asm volatile("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "=v"(r) : "v"(v), "v"(x), "i"(n));
+  return r;
+}
+template <int n>
+__device__ __forceinline__ void fmac_bcast(float& acc, float v, float x) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc) : "v"(v), "v"(x), "i"(n));
+}
+
+// the scan's update for states n .. kStates - 1 with broadcast row operands (bb: lane i of every
+// row holds b[i], bc: c[i])
+template <int n>
+struct DppStates {
+  static __device__ __forceinline__ void run(float (&h)[kStates], const float (&a2)[kStates],
+                                             float delta, float u, float bb, float bc, float& y0,
+                                             float& y1) {
+    if constexpr (n < kStates) {
+      const float e = __builtin_amdgcn_exp2f(delta * a2[n]);
+      const float inj = mul_bcast<n>(bb, u);
+      h[n] = fmaf(e, h[n], inj);
+      if (n & 1) fmac_bcast<n>(y1, bc, h[n]);
+      else fmac_bcast<n>(y0, bc, h[n]);
+      DppStates<n + 1>::run(h, a2, delta, u, bb, bc, y0, y1);
+    }
+  }
+};
 
 // out[kOutPerWave * wave + {0 .. 5}] = clock before, clock after, real time before, after, the
 // HW_ID register (SIMD, CU, shader array and engine of the wave) and the XCC_ID register;
@@ -136,6 +172,27 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int iters, float s, co
       for (int v = 0; v < 16; ++v) result += m[j][v];
 #pragma unroll
     for (int j = 0; j < kStates; ++j) result += acc[j];
+  } else if constexpr (OP == kScanDpp) {
+    // as kScanUpdate, with the rows held in VGPRs (lane i of every 16-lane row holds b[i] and
+    // c[i]) and read as DPP broadcast operands instead of SGPRs
+    float a2[kStates];
+#pragma unroll
+    for (int j = 0; j < kStates; ++j) a2[j] = -(1.0f + 0.5f * j) * (1.0f + 0.001f * a);
+    const float bb = 0.5f + 0.01f * (threadIdx.x & 15), bc = 0.25f + 0.02f * (threadIdx.x & 15);
+    float delta = 0.05f + 0.01f * b, u = a, ysum = 0.f;
+    stamp(c0, r0);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int t = 0; t < kTokens; ++t) {
+        float y0 = 0.f, y1 = 0.f;
+        DppStates<0>::run(acc, a2, delta, u, bb, bc, y0, y1);
+        ysum += y0 + y1;
+        u = fmaf(u, 0.999f, 1e-4f);
+        delta = fmaf(delta, 0.999f, 1e-4f);
+      }
+    }
+    stamp(c1, r1);
+    result = ysum;
   } else if constexpr (OP == kScanUpdate) {
     // per token, delta and u change, and every state n does
     //   e = 2^(delta * a2[n]); inj = u * b[n]; h[n] = e h[n] + inj; y += h[n] c[n]
@@ -193,6 +250,8 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int iters, float s, co
             if (j & 1) acc[j] = fmaf(a, b, acc[j]);
             else acc[j] = __builtin_amdgcn_exp2f(-acc[j]);
           }
+          else if constexpr (OP == kMulDpp) acc[j] = mul_bcast<3>(cm, acc[j]);
+          else if constexpr (OP == kFmacDpp) fmac_bcast<5>(acc[j], a, b);
           else acc[j] = __builtin_amdgcn_exp2f(-acc[j]);   // converges; never overflows
         }
     }
@@ -223,12 +282,12 @@ extern "C" {
 int attamba_probe_ops_per_iter(int op) {
   switch (op) {
     case kFmaV: case kFmaS: case kMulV: case kExp: case kFmacV: case kFmacS: case kAddV:
-    case kFmamk: case kCvtPk: case kDot2: return kChains * kUnroll;
+    case kFmamk: case kCvtPk: case kDot2: case kMulDpp: case kFmacDpp: return kChains * kUnroll;
     case kExpMul: return kChains * kUnroll;            // exp + mul pairs
     case kExpFmac: return kChains * kUnroll / 2;       // exp + fmac pairs
     case kMfma: case kMfmaFmac: case kMfmaExp: case kMfmaFma3:
       return kMfmaChains * kUnroll / 2;   // MFMAs (each with 8 VALU instructions beside it)
-    case kScanUpdate: return kStates * kTokens;   // state updates per iteration
+    case kScanUpdate: case kScanDpp: return kStates * kTokens;   // state updates per iteration
     default: return -1;
   }
 }
@@ -264,6 +323,9 @@ int attamba_probe_issue(int op, int blocks, int iters, float s, const float* vin
     case kMfmaFmac: hipLaunchKernelGGL(issue_probe_kernel<kMfmaFmac>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
     case kMfmaExp: hipLaunchKernelGGL(issue_probe_kernel<kMfmaExp>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
     case kMfmaFma3: hipLaunchKernelGGL(issue_probe_kernel<kMfmaFma3>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
+    case kMulDpp: hipLaunchKernelGGL(issue_probe_kernel<kMulDpp>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
+    case kFmacDpp: hipLaunchKernelGGL(issue_probe_kernel<kFmacDpp>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
+    case kScanDpp: hipLaunchKernelGGL(issue_probe_kernel<kScanDpp>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
     default: return 1;
   }
   return static_cast<int>(hipGetLastError());
