@@ -13,7 +13,7 @@
 // Workgroup = 8 waves (2 per SIMD), tile 256 features x 256 tokens, K steps of 64; wave
 // (wf, wt) owns 64 features x 128 tokens as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16. Both
 // operands are K-contiguous, so every operand is one ds_read_b128 from an LDS tile whose 16-byte
-// segments are XOR-swizzled by row (conflict-free for 8 consecutive rows). Tiles come from HBM
+// segments are XOR-swizzled by row (conflict-free for 16 consecutive rows). Tiles come from HBM
 // straight into LDS (global_load_lds_dwordx4) into two buffers (128 KB, one workgroup per CU),
 // one barrier per K step. The large tile halves the bytes each CU pulls from L2 per FLOP
 // against 128 x 128 tiles, whose data-return path was busy 83 % of the time.
@@ -36,8 +36,12 @@ constexpr int NT = NW * 64; // threads per workgroup
 constexpr int kChunks = TM * TK * 2 / 1024;     // 1 KB chunks per operand tile (32)
 constexpr int kChunksPerWave = kChunks / NW;    // 4
 
-// element offset of logical 16-byte segment s of tile row r (8 segments per row)
-__device__ __forceinline__ int seg_off(int r, int s) { return r * TK + 8 * (s ^ (r & 7)); }
+// element offset of logical 16-byte segment s of tile row r (8 segments per row). The LDS
+// serves a ds_read_b128 16 lanes at a time from 64 four-byte banks (256 bytes): the 16 lanes
+// that read one segment of 16 consecutive rows must hit 16 distinct 16-byte slots of that
+// window. Rows of 128 bytes alternate between its two halves, so the swizzle takes row bits
+// 1..3 (bits 0..2 put rows r and r + 8 on one slot: 4 conflict cycles on every read).
+__device__ __forceinline__ int seg_off(int r, int s) { return r * TK + 8 * (s ^ ((r >> 1) & 7)); }
 
 struct ProjTile {
   __bf16 w[2][TM * TK];
@@ -66,14 +70,14 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
   const __bf16* X = static_cast<const __bf16*>(p.x);
 
   // LDS-direct copies: lane l of chunk ch fills slot ch * 64 + l = (row 8 ch + l / 8, physical
-  // segment l % 8), which holds logical segment (l % 8) ^ (row & 7). Rows past the matrix
+  // segment l % 8), which holds logical segment (l % 8) ^ ((row >> 1) & 7). Rows past the matrix
   // re-read its last row (their results are not stored).
   int woff[kChunksPerWave], xoff[kChunksPerWave];
 #pragma unroll
   for (int i = 0; i < kChunksPerWave; ++i) {
     const int ch = wid * kChunksPerWave + i;
     const int r = 8 * ch + lane / 8;
-    const int s = (lane % 8) ^ (r & 7);
+    const int s = (lane % 8) ^ ((r >> 1) & 7);
     woff[i] = min(f0 + r, p.n_out - 1) * d + 8 * s;
     xoff[i] = min(t0 + r, p.T - 1) * d + 8 * s;
   }
