@@ -16,13 +16,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 64;    // keys per tile
 
-// Row r of a tile keeps its 16-byte segment s at position s ^ swz(r). The K read (16 lanes,
-// one segment, 16 consecutive rows) and the transposing V read (16 lanes, two adjacent
-// segments, 4 consecutive rows starting at a multiple of 4) then touch distinct bank groups.
+// Row r of a tile keeps its 16-byte segment s at position s ^ swz(r). The LDS has 64 banks of
+// 4 bytes (a 256-byte window); a ds_read_b128 is served 16 lanes per pass, a ds_read_b64 32
+// lanes per pass. Both reads then touch distinct banks in every pass:
+// - the K read: 16 lanes, one segment of 16 consecutive rows;
+// - the transposing V read: 32 lanes, the four segments 4j .. 4j + 3 of 4 consecutive rows
+//   starting at a multiple of 4 (256 bytes).
+// At hd 64 a row is half the window (rows alternate halves): swz must differ between the 8 rows
+// of one parity in an aligned group of 16, and its bit 2 between rows r and r + 2 of an aligned
+// group of 4. At hd 128 a row fills the window: swz must differ over 16 consecutive rows, and its
+// bits 2..3 over an aligned group of 4. (The earlier swizzle left the V read 2-way conflicted.)
 template <int HD>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (HD == 64) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-  else return 2 * (r & 7) + ((r >> 3) & 1);
+  if constexpr (HD == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 // max of x over lanes q and q + 32 (the two key halves of one query): v_permlane32_swap
