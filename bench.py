@@ -242,7 +242,21 @@ def bench_prefill(args):
         step()
     torch.cuda.synchronize()
     extra_warmup = clock_warmup(step, torch)
-    # The same steps with the caches flushed before each one (a 512 MiB write evicts the L2s and
+    # Whole-job timing: exactly K steps, synchronised on both sides, right after the clock
+    # warm-up. HIP events recorded on the launch stream between the kernels of these same steps
+    # give the per-kernel durations.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    # Then the same steps with the caches flushed before each one (a 512 MiB write evicts the L2s and
     # the 256 MB MALL, which can otherwise hold a small configuration's whole working set).
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     evf = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -256,19 +270,6 @@ def bench_prefill(args):
                               "chunk_attn": round(float(np.mean([e[2].elapsed_time(e[3]) for e in evf])) * 1e3, 2)},
                "step_us": round(float(np.mean([e[0].elapsed_time(e[3]) for e in evf])) * 1e3, 2),
                "note": "HIP events around each step after a 512 MiB device write; value and kernels_us are hot"}
-    # Whole-job timing: exactly K steps, synchronised on both sides. HIP events recorded on the
-    # launch stream between the kernels of these same steps give the per-kernel durations.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    seg_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-
     ms = wall * 1e3 / args.steps
     tok_s = T / (wall / args.steps)
     pairs = attention_pairs(inp.seq_cu, lay0.chunk_cu.cpu().numpy(), lay0.token_chunk.cpu().numpy(),
