@@ -276,15 +276,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(N == 16 &
           dts[j] = dt.load(rd, c);
           if (gated) zs[j] = z.load(rd, c);
         }
-        typename SsmLane<T, N>::Rows rn, rc;
-        SsmLane<T, N>::load_rows(bm + bs * N, cm + bs * N, rn);
+        // two row sets used in turn (token j reads set j & 1 and requests the next token's
+        // rows into the other): with the per-token guards, copying one set into the other
+        // would cost 16 scalar moves per token
+        typename SsmLane<T, N>::Rows rr[2];
+        SsmLane<T, N>::load_rows(bm + bs * N, cm + bs * N, rr[0]);
 #pragma unroll
         for (int j = 0; j < PU; ++j) {
           if (j < nb) {
             const int t = bs + j;
-            rc = rn;
+            const typename SsmLane<T, N>::Rows& rc = rr[j & 1];
             rows_ready(rc.b[0], rc.c[0]);
-            if (j + 1 < nb) SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rn);
+            if (j + 1 < nb) SsmLane<T, N>::load_rows(bm + (t + 1) * N, cm + (t + 1) * N, rr[(j + 1) & 1]);
             order_point();
             const float xin = conv ? cv.next(win, xs[j]) : xs[j];
             if (j == 0 && bs == cs) out = s.template step<true>(xin, dts[j], rc);
