@@ -18,10 +18,13 @@
 // one barrier per K step. The large tile halves the bytes each CU pulls from L2 per FLOP
 // against 128 x 128 tiles, whose data-return path was busy 83 % of the time.
 // Within a K step the operands of k-slice ks + 1 are read from LDS while slice ks's eight
-// products run, one read after each product (two register stages, 224 VGPRs, still two waves
-// per SIMD); slice 3's products run after the barrier, beside the reads of the next step's
-// slice 0 and the copies of the step after it. Without this the wave waited for each slice's
-// reads before its products: 910 against 978 TFLOP/s.
+// products run, one read after each of the first six products, in an order fixed by
+// scheduling barriers (two register stages, 222 VGPRs, still two waves per SIMD); slice 3's
+// products run after the barrier, beside the reads of the next step's slice 0 and the copies
+// of the step after it. Without this the wave waited for each slice's reads before its
+// products: 910 against 978 TFLOP/s. The epilogue finds each feature group's output segment
+// on the scalar unit (a per-lane search had read the output pointers with 64 dependent vector
+// loads per wave and tile: 911 against 977 TFLOP/s).
 #include "common.h"
 #include "kernels.h"
 #include <type_traits>
@@ -127,13 +130,6 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[st][j] = *reinterpret_cast<const bf16x8*>(sx + boff[j][ks]);
   };
-  auto mm = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st][i], b[st][j], acc[i][j], 0, 0, 0);
-  };
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -143,38 +139,34 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
   // One K step. The scheduling groups pin the order: a product, then one LDS read of the next
   // slice (0x008 = MFMA, 0x100 = LDS read). ISSUE: copy step kt + 2 into the buffer just freed;
   // RD: read slice 0 of step kt + 1 (both compile-time, so the loop body has no branches).
-  auto interleave = [] {
+  // One slice's eight products in a fixed order (each accumulator again 8 products later),
+  // with the next slice's six operand reads placed after the first six of them; scheduling
+  // barriers keep the order as written.
+  auto slice = [&](int st, int buf_next, int ks_next, bool read_next) {
+    const int nt = st ^ 1;
+    const __bf16* sw = sm.w[buf_next];
+    const __bf16* sx = sm.x[buf_next];
 #pragma unroll
-    for (int r = 0; r < 6; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int u = 0; u < 8; ++u) {
+      const int i = u >> 2, j = u & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st][i], b[st][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (read_next && u < 6) {
+        if (u < 2) a[nt][u] = *reinterpret_cast<const bf16x8*>(sw + aoff[u][ks_next]);
+        else b[nt][u - 2] = *reinterpret_cast<const bf16x8*>(sx + boff[u - 2][ks_next]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
   };
   auto body = [&](int kt, auto ISSUE, auto RD) {
     const int buf = kt & 1;
-    rd(1, buf, 1);
-    mm(0);
-    interleave();
-    rd(0, buf, 2);
-    mm(1);
-    interleave();
-    rd(1, buf, 3);
-    mm(0);
-    interleave();
+    slice(0, buf, 1, true);
+    slice(1, buf, 2, true);
+    slice(0, buf, 3, true);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's reads of buf and its copies of step kt + 1 are done ...
     __syncthreads();                 // ... and every wave's
-    if constexpr (decltype(RD)::value) rd(0, buf ^ 1, 0);
     if constexpr (decltype(ISSUE)::value) issue((kt + 2) * TK, buf);
-    mm(1);
-    if constexpr (decltype(RD)::value) {
-#pragma unroll
-      for (int r = 0; r < 6; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-    }
+    slice(1, buf ^ 1, 0, decltype(RD)::value);
     __builtin_amdgcn_sched_barrier(0);
   };
   using yes = std::integral_constant<bool, true>;
@@ -188,7 +180,50 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
   body(kt, no{}, no{});
 
   // epilogue: block (i, j), register group g: token t0 + 128 wt + 32 j + q, features
-  // f0 + 64 wf + 32 i + 8 g + 4 hf .. +3 (all four in one output segment)
+  // f0 + 64 wf + 32 i + 8 g + 4 hf .. +3 (all four in one output segment). The wave's groups of
+  // 4 features are visited in increasing order, so the segment holding them is found by walking
+  // the segment boundaries forward on the scalar unit (one compare per group; constant indices
+  // into the parameter block when a boundary is crossed); each lane takes its half's segment.
+  int sk = 0;                                          // segment of the current feature
+  int s_next = p.n_seg > 1 ? p.seg_start[1] : p.n_out;  // its end
+  auto seg_at = [&](int k, __bf16*& out, int& s0, int& end) {
+#pragma unroll
+    for (int m = 0; m < kMaxProjSegments; ++m)
+      if (m == k) {
+        out = static_cast<__bf16*>(p.out[m]);
+        s0 = p.seg_start[m];
+        end = p.seg_start[m + 1];
+      }
+  };
+  __bf16* s_out = static_cast<__bf16*>(p.out[0]);
+  int s_s0 = 0;
+  auto advance = [&](int f) {
+    while (f >= s_next && sk + 1 < p.n_seg) {
+      ++sk;
+      seg_at(sk, s_out, s_s0, s_next);
+    }
+  };
+  // per-lane destination of each of the 8 feature groups, then the stores token block by
+  // token block (the 8 stores of one block complete the wave's 128-byte row pieces together)
+  __bf16* gout[2][4];
+  int gcol[2][4], gwid[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int fb = f0 + wf * 64 + 32 * i + 8 * g;
+      gout[i][g] = nullptr;
+      gcol[i][g] = 0;
+      gwid[i][g] = 0;
+      if (fb >= p.n_out) continue;
+      advance(fb);
+      __bf16* const out_a = s_out;
+      const int col_a = fb - s_s0, w_a = s_next - s_s0;
+      advance(fb + 4);
+      gout[i][g] = hf ? s_out : out_a;
+      gcol[i][g] = hf ? fb + 4 - s_s0 : col_a;
+      gwid[i][g] = hf ? s_next - s_s0 : w_a;
+    }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = t0 + wt * 128 + 32 * j + q;
@@ -199,16 +234,10 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
       for (int g = 0; g < 4; ++g) {
         const int f = f0 + wf * 64 + 32 * i + 8 * g + 4 * hf;
         if (f >= p.n_out) continue;
-        int sgi = 0;
-#pragma unroll
-        for (int k = 1; k < kMaxProjSegments; ++k)
-          if (k < p.n_seg && f >= p.seg_start[k]) sgi = k;
-        const int s0 = p.seg_start[sgi], width = p.seg_start[sgi + 1] - s0;
         bf16x4 vv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) vv[e] = static_cast<__bf16>(acc[i][j][4 * g + e]);
-        __bf16* dst = static_cast<__bf16*>(p.out[sgi]) + static_cast<size_t>(t) * width + (f - s0);
-        *reinterpret_cast<bf16x4*>(dst) = vv;
+        *reinterpret_cast<bf16x4*>(gout[i][g] + static_cast<size_t>(t) * gwid[i][g] + gcol[i][g]) = vv;
       }
   }
 }
