@@ -573,6 +573,7 @@ def bench_train(args):
                                       act["q"].dtype)
 
     def step(ev=None):
+        stream = torch.cuda.current_stream()
         if ev is not None:
             ev[0].record(stream)
         res = prefill_forward(act, par, inp.seq_cu, H, hd, cfg.P, cfg.layer_idx, cfg.L,
@@ -602,6 +603,26 @@ def bench_train(args):
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
+    eager_wall = time.perf_counter() - t0
+    # The same step captured once as a HIP graph (the step makes about twenty allocations and a
+    # dozen launches through Python, which can take as long as the GPU work) and replayed K
+    # times; tests/test_gpu_graph.py checks the replays against eager steps.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    for _ in range(min(args.warmup, 50)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for e in evs:
@@ -629,6 +650,8 @@ def bench_train(args):
                      "avg_launch_us": round(sbwd_ms * 1e3, 2)},
         "phases_us": {"forward": round(fwd_ms * 1e3, 2), "attention_backward": round(abwd_ms * 1e3, 2),
                       "scan_backward": round(sbwd_ms * 1e3, 2)},
+        "timing": "K replays of the step captured as a HIP graph",
+        "eager_ms_per_step": round(eager_wall * 1e3 / args.steps, 4),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_train(cfg, inp, dout_h, T)
