@@ -331,7 +331,8 @@ int attamba_decode_load_prefix(attamba_decode_cache* cache, const attamba_decode
  * All pointers are device pointers owned by the caller; nothing is allocated.
  * Errors: NULL_ARG (x, w or a used out[i]); BAD_SHAPE (T < 0, d < 64 or not a multiple of 64,
  * n_out < 1, n_seg outside 1..ATTAMBA_PROJ_MAX_SEGMENTS, seg_start not starting at 0, not
- * increasing, not ending at n_out, or a segment start not a multiple of 4); UNSUPPORTED (dtype
+ * increasing, not ending at n_out, or a segment start or end not a multiple of 4, so n_out too
+ * must be one); UNSUPPORTED (dtype
  * other than bf16, or T*d, n_out*d or T*n_out at or above 2^31); HIP.
  * ---------------------------------------------------------------------------------------- */
 #define ATTAMBA_PROJ_MAX_SEGMENTS 12

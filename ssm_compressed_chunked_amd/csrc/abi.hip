@@ -288,9 +288,10 @@ int attamba_input_proj(const attamba_proj_args* a, attamba_stream_t stream) {
     return fail(ATTAMBA_ERR_BAD_SHAPE, "input_proj: T=%d d=%d n_out=%d n_seg=%d", a->T, a->d, a->n_out, a->n_seg);
   if (a->seg_start[0] != 0 || a->seg_start[a->n_seg] != a->n_out)
     return fail(ATTAMBA_ERR_BAD_SHAPE, "input_proj: segments must cover features 0 .. n_out");
+  // every segment start and end a multiple of 4: the kernels store 4 features (8 bytes) at once
   for (int i = 0; i < a->n_seg; ++i)
-    if (a->seg_start[i + 1] <= a->seg_start[i] || a->seg_start[i] % 4 != 0)
-      return fail(ATTAMBA_ERR_BAD_SHAPE, "input_proj: segment %d (start %d, end %d) empty or start not a multiple of 4",
+    if (a->seg_start[i + 1] <= a->seg_start[i] || a->seg_start[i] % 4 != 0 || a->seg_start[i + 1] % 4 != 0)
+      return fail(ATTAMBA_ERR_BAD_SHAPE, "input_proj: segment %d (start %d, end %d) empty or not on multiples of 4",
                   i, a->seg_start[i], a->seg_start[i + 1]);
   if (static_cast<int64_t>(a->T) * a->d > INT32_MAX || static_cast<int64_t>(a->n_out) * a->d > INT32_MAX ||
       static_cast<int64_t>(a->T) * a->n_out > INT32_MAX)

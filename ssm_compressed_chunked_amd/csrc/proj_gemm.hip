@@ -25,6 +25,8 @@
 // products: 910 against 978 TFLOP/s. The epilogue finds each feature group's output segment
 // on the scalar unit (a per-lane search had read the output pointers with 64 dependent vector
 // loads per wave and tile: 911 against 977 TFLOP/s).
+// A last feature tile of at most 64 features (the 4 N rows of Bm/Cm at the prefill shape) goes
+// to a separate tail kernel (below) instead of a mostly empty 256 x 256 tile.
 #include "common.h"
 #include "kernels.h"
 #include <type_traits>
@@ -242,13 +244,137 @@ __global__ __launch_bounds__(NT) void proj_gemm_kernel(ProjParams p) {
   }
 }
 
+// Features f_lo .. n_out - 1 when they are the at most kTailMax features of a last, partial
+// feature tile. As a tile of their own they would cost a whole tile's products for a quarter
+// of its outputs or less, and at the prefill shape (24 full feature tiles x 64 token tiles =
+// 6 rounds of one workgroup per CU) a seventh round: 404 us against 370 us for the 24 full
+// tiles alone. The tail streams x once more for 64 features, so it is bound by that read.
+// A 4-wave workgroup takes 64 features x 64 tokens, each wave one 32 x 32 block of
+// v_mfma_f32_32x32x16_bf16; the K steps of 64 come into LDS by LDS-direct copies (the same
+// swizzled layout as the large tiles) into a ring of kTailStages buffers, so that the copies of
+// the next seven steps are in flight while one step's four products run (with two buffers the
+// copy latency was exposed at every step: 23 us; now 15-17 us at the prefill shape).
+constexpr int kTailMax = 64;
+// s_waitcnt immediate: at most n vector-memory operations of this wave outstanding
+constexpr int vmcnt_le(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+constexpr int kTailTokens = 64;
+constexpr int kTailStages = 8;
+
+struct TailTile {
+  __bf16 w[kTailStages][kTailMax * TK];
+  __bf16 x[kTailStages][kTailTokens * TK];
+};
+
+__global__ __launch_bounds__(256) void proj_tail_kernel(ProjParams p, int f_lo) {
+  __shared__ TailTile sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane & 31, hf = lane >> 5;
+  const int fb = wid & 1, tb = wid >> 1;           // 32-feature block, 32-token block
+  const int t0 = blockIdx.x * kTailTokens;
+  const int d = p.d;
+  const __bf16* W = static_cast<const __bf16*>(p.w);
+  const __bf16* X = static_cast<const __bf16*>(p.x);
+  // copies: wave w fills 1 KB chunks w and w + 4 of each 8 KB tile (8 rows of 128 bytes each);
+  // lane l holds row 8 ch + l / 8, physical segment l % 8 = logical segment (l % 8) ^ ((row >> 1) & 7)
+  int woff[2], xoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = wid + 4 * i;
+    const int r = 8 * ch + lane / 8;
+    const int sg = (lane % 8) ^ ((r >> 1) & 7);
+    woff[i] = min(f_lo + r, p.n_out - 1) * d + 8 * sg;
+    xoff[i] = min(t0 + r, p.T - 1) * d + 8 * sg;
+  }
+  auto issue = [&](int k0, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = wid + 4 * i;
+      __builtin_amdgcn_global_load_lds(W + woff[i] + k0, LDS_PTR(void, sm.w[buf] + ch * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(X + xoff[i] + k0, LDS_PTR(void, sm.x[buf] + ch * 512), 16, 0, 0);
+    }
+  };
+  const int nk = d / TK;
+  constexpr int kLoads = 4;          // copies per wave and step
+  f32x16 acc = {};
+  for (int s = 0; s < kTailStages - 1; ++s)
+    if (s < nk) issue(s * TK, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % kTailStages;
+    // this wave's copies of step kt have landed (those of the later steps issued so far may
+    // still fly) ...
+    const int later = min(nk - 1 - kt, kTailStages - 2);
+    if (later >= 6) __builtin_amdgcn_s_waitcnt(vmcnt_le(6 * kLoads));
+    else if (later == 5) __builtin_amdgcn_s_waitcnt(vmcnt_le(5 * kLoads));
+    else if (later == 4) __builtin_amdgcn_s_waitcnt(vmcnt_le(4 * kLoads));
+    else if (later == 3) __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * kLoads));
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * kLoads));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(1 * kLoads));
+    else __builtin_amdgcn_s_waitcnt(0);
+    // ... and every wave's, and every wave is done with step kt - 1's buffer. A bare barrier:
+    // the fence of __syncthreads would also wait for the later steps' copies.
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + kTailStages - 1 < nk) issue((kt + kTailStages - 1) * TK, (kt + kTailStages - 1) % kTailStages);
+    bf16x8 a[TK / 16], b[TK / 16];   // the step's operands, all read before its products
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      a[ks] = *reinterpret_cast<const bf16x8*>(sm.w[buf] + seg_off(32 * fb + q, 2 * ks + hf));
+      b[ks] = *reinterpret_cast<const bf16x8*>(sm.x[buf] + seg_off(32 * tb + q, 2 * ks + hf));
+    }
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], acc, 0, 0, 0);
+  }
+
+  // accumulator register 4 gq + e: feature f_lo + 32 fb + 8 gq + 4 hf + e, token t0 + 32 tb + q;
+  // the four features of a group lie in one segment (segments start and end on multiples of 4)
+  const int t = t0 + 32 * tb + q;
+  if (t >= p.T) return;
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    const int f = f_lo + 32 * fb + 8 * gq + 4 * hf;
+    if (f >= p.n_out) continue;
+    int sel = 0;
+#pragma unroll
+    for (int m = 1; m < kMaxProjSegments; ++m)
+      if (m < p.n_seg && f >= p.seg_start[m]) sel = m;
+    __bf16* out = nullptr;
+    int s_lo = 0, width = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxProjSegments; ++m)
+      if (m == sel) {
+        out = static_cast<__bf16*>(p.out[m]);
+        s_lo = p.seg_start[m];
+        width = p.seg_start[m + 1] - s_lo;
+      }
+    bf16x4 vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = static_cast<__bf16>(acc[4 * gq + e]);
+    *reinterpret_cast<bf16x4*>(out + static_cast<size_t>(t) * width + (f - s_lo)) = vv;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_proj_gemm(const ProjParams& p, hipStream_t stream) {
   if (p.T == 0 || p.n_out == 0) return hipSuccess;
-  const int grid = 8 * ceil_div(p.n_out, TM) * ceil_div(ceil_div(p.T, TN), 8);
-  hipLaunchKernelGGL(proj_gemm_kernel, dim3(grid), dim3(NT), 0, stream, p);
-  return hipGetLastError();
+  // a last feature tile with at most kTailMax features goes to the tail kernel
+  const int rem = p.n_out % TM;
+  const bool tail = rem > 0 && rem <= kTailMax;
+  const int n_ft = tail ? p.n_out / TM : ceil_div(p.n_out, TM);
+  if (n_ft > 0) {
+    const int grid = 8 * n_ft * ceil_div(ceil_div(p.T, TN), 8);
+    hipLaunchKernelGGL(proj_gemm_kernel, dim3(grid), dim3(NT), 0, stream, p);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (tail) {
+    hipLaunchKernelGGL(proj_tail_kernel, dim3(ceil_div(p.T, kTailTokens)), dim3(256), 0, stream, p,
+                       p.n_out - rem);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace attamba

@@ -144,7 +144,9 @@ def test_input_proj_validates_before_launch():
     a.seg_start[1] = 16
     a.seg_start[2] = 20
     assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # does not reach n_out
-    a.seg_start[2] = 24
+    a.n_out = a.seg_start[2] = 22
+    assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # end not 4-aligned
+    a.n_out = a.seg_start[2] = 24
     a.n_seg = B.PROJ_MAX_SEGMENTS + 1
     assert lib.attamba_input_proj(C.byref(a), None) == B.ERR_BAD_SHAPE      # too many segments
     a.n_seg = 2

@@ -507,6 +507,10 @@ def test_attention_growing_scores(hd, mode, L):
     (129, 64, [64, 4, 60]),                         # feature segments inside one tile
     (1, 256, [256]),
     (517, 192, [192, 192, 192, 32, 32, 32, 32, 4]),  # N = 32, eight segments, ragged both ways
+    # a last feature tile of at most 64 features goes to the tail kernel
+    (300, 128, [256, 16, 16, 16, 16]),              # 64 past the full tile, as at the prefill shape
+    (517, 192, [512, 4, 32, 8]),                    # 44 past two full tiles, ragged tokens
+    (77, 64, [20, 8]),                              # no full tile at all
 ])
 def test_input_proj_elementwise(T, d, widths):
     say(f"input_proj T={T} d={d} widths={widths}")
