@@ -434,7 +434,7 @@ def bench_proj(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "proj_bf16", "T": T, "d": d, "n_out": n_out,
                    "segments": inp.widths},
-        "roofline": {"bound": "mfma", "kernel": "proj_gemm_kernel", "achieved": round(tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "proj_gemm_kernel + proj_tail_kernel (one call)", "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
