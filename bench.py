@@ -327,6 +327,12 @@ def bench_prefill(args):
                       "frac_of_2.5PF": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                       "traffic": None if attn_traffic is None else attn_traffic["bytes_per_launch"]},
     }
+    mp = measured_peaks()
+    if mp.get("copy_GBps"):
+        mp["scan_frac_of_copy"] = round(scan_gbps / mp["copy_GBps"], 4)
+    if mp.get("mfma_bf16_TFLOPs"):
+        mp["attn_frac_of_mfma"] = round(attn_tflops / mp["mfma_bf16_TFLOPs"], 4)
+    line["measured_peaks"] = mp
     if not args.no_cpu_baseline and not with_block:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, T)
     print(json.dumps(line), flush=True)
@@ -392,6 +398,10 @@ def bench_decode(args):
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                          "traffic": None if traffic is None else traffic["bytes_per_launch"],
                          "algorithmic_bytes_per_step": round((kv_bytes + state_bytes) / cfg.steps)}}
+    mp = measured_peaks(want_mfma=False)
+    if mp.get("read_GBps"):
+        mp["decode_frac_of_read"] = round(gbps / mp["read_GBps"], 4)
+    line["measured_peaks"] = mp
     print(json.dumps(line), flush=True)
 
 
@@ -427,6 +437,9 @@ def bench_proj(args):
     flop = 2.0 * T * d * n_out
     tflops = flop / (us * 1e-6) / 1e12
     traffic = measured_traffic("proj_gemm_kernel", ["proj_gemm.hip", "common.h"], args.workload)
+    mp = measured_peaks(want_copy=False)
+    if mp.get("mfma_bf16_TFLOPs"):
+        mp["proj_frac_of_mfma"] = round(tflops / mp["mfma_bf16_TFLOPs"], 4)
     print(json.dumps({
         "metric": "input projections TFLOP/s (x W^T, bf16)", "value": round(tflops, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -438,7 +451,8 @@ def bench_proj(args):
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                     "avg_launch_us": round(us, 2)}}), flush=True)
+                     "avg_launch_us": round(us, 2)},
+        "measured_peaks": mp}), flush=True)
 
 
 def bench_layer(args):
@@ -661,6 +675,93 @@ def bench_train(args):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_train(cfg, inp, dout_h, T)
     print(json.dumps(line), flush=True)
+
+
+def measured_peaks(want_copy=True, want_mfma=True) -> dict:
+    """The denominators measured on this machine, reported beside the vendor peaks: the bandwidth
+    of a plain 512 MiB device copy (read plus write bytes over the event-timed copy) and of a
+    read-only stream over 2 GiB (the probe library's streaming-read kernel), and the
+    bf16 matrix-core rate of the issue probe's MFMA loop (v_mfma_f32_32x32x16_bf16 chains,
+    two waves on every SIMD, 32 768 FLOP per instruction) over its event-timed launch."""
+    import ctypes
+    import torch
+    out = {}
+    stream = torch.cuda.current_stream()
+    if want_copy:
+        nbytes = 512 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["copy_GBps"] = round(2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del src, dst
+        # a read-only stream over 2 GiB (the probe library's streaming-read kernel): the
+        # denominator of kernels that mostly read
+        if os.path.exists(PROBE_LIB):
+            lib = ctypes.CDLL(PROBE_LIB)
+            lib.attamba_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+            big = torch.ones(4 * nbytes // 4, dtype=torch.float32, device="cuda")
+            blocks = torch.cuda.get_device_properties(0).multi_processor_count * 8
+            sink = torch.empty(256 * blocks, dtype=torch.float32, device="cuda")
+
+            def read_once():
+                rc = lib.attamba_probe_read_stream(big.data_ptr(), 4 * nbytes, sink.data_ptr(),
+                                                   blocks, ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"read-stream probe failed ({rc})")
+            for _ in range(3):
+                read_once()
+            e0.record(stream)
+            for _ in range(reps):
+                read_once()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out["read_GBps"] = round(4 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+            del big, sink
+    if want_mfma:
+        if not os.path.exists(PROBE_LIB):
+            out["mfma_bf16_TFLOPs"] = None
+            out["mfma_note"] = f"{os.path.basename(PROBE_LIB)} not built"
+        else:
+            lib = ctypes.CDLL(PROBE_LIB)
+            lib.attamba_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p]
+            lib.attamba_probe_ops_per_iter.argtypes = [ctypes.c_int]
+            op, W = 4, 2                       # the MFMA loop; two waves per SIMD
+            blocks = torch.cuda.get_device_properties(0).multi_processor_count * W
+            vin = torch.full((192,), 0.75, dtype=torch.float32, device="cuda")
+            rows = (ctypes.c_float * 32)(*([0.5] * 32))
+            probe_out = torch.zeros(6 * 4 * blocks, dtype=torch.int64, device="cuda")
+            sink = torch.empty(256 * blocks, dtype=torch.float32, device="cuda")
+            iters = PROBE_ITERS[op]
+
+            def launch():
+                rc = lib.attamba_probe_issue(op, blocks, iters, 0.3, vin.data_ptr(), rows,
+                                             probe_out.data_ptr(), sink.data_ptr(),
+                                             ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"probe launch failed ({rc})")
+            for _ in range(2):
+                launch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 3
+            e0.record(stream)
+            for _ in range(reps):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mfmas = blocks * 4 * lib.attamba_probe_ops_per_iter(op) * iters * reps
+            out["mfma_bf16_TFLOPs"] = round(mfmas * 32768.0 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    return out
 
 
 def bench_copy(args):

@@ -274,6 +274,29 @@ __global__ __launch_bounds__(256) void issue_probe_kernel(int iters, float s, co
   }
 }
 
+// Streaming read: each step a workgroup reads one contiguous block of kReadUnroll x 256 16-byte
+// pieces (thread t takes pieces t, t + 256, ...: eight loads in flight per thread, each load
+// instruction covering 1 KB per wave), then moves on by the grid's span; every thread writes one
+// value, so no load is dropped. The host times the launch with events; bytes / time is the read
+// bandwidth a kernel that only reads can reach.
+constexpr int kReadUnroll = 8;
+__global__ __launch_bounds__(256) void read_stream_kernel(const uint4* __restrict__ buf, size_t n16,
+                                                          float* __restrict__ sink) {
+  constexpr size_t kStep = kReadUnroll * 256;
+  const size_t span = static_cast<size_t>(gridDim.x) * kStep;
+  uint32_t acc = 0;
+  size_t base = static_cast<size_t>(blockIdx.x) * kStep;
+  for (; base + kStep <= n16; base += span) {
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) v[k] = buf[base + k * 256 + threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) acc += v[k].x ^ v[k].w;
+  }
+  for (size_t i = base + threadIdx.x; i < n16; i += 256) acc += buf[i].x;   // the last partial block
+  sink[static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x] = static_cast<float>(acc);
+}
+
 }  // namespace
 
 extern "C" {
@@ -328,6 +351,18 @@ int attamba_probe_issue(int op, int blocks, int iters, float s, const float* vin
     case kScanDpp: hipLaunchKernelGGL(issue_probe_kernel<kScanDpp>, grid, block, 0, stream, iters, s, vin, rows, out, sink); break;
     default: return 1;
   }
+  return static_cast<int>(hipGetLastError());
+}
+
+// Reads `bytes` (a multiple of 16, 16-byte aligned) of device memory once with `blocks`
+// workgroups of 256 threads; sink: blocks * 256 floats on the device. Returns 0 or a HIP error
+// code; 1 for bad arguments.
+int attamba_probe_read_stream(const void* buf, size_t bytes, float* sink, int blocks,
+                              hipStream_t stream) {
+  if (!buf || !sink || blocks < 1 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return 1;
+  hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(buf), bytes / 16, sink);
   return static_cast<int>(hipGetLastError());
 }
 
